@@ -1,0 +1,184 @@
+/*
+ * taq.h - tiled causal attention over a grouped-quantized KV cache, for
+ * AMD Instinct MI355X (gfx950).  Plain C ABI: every pointer is a plain host or
+ * device address, every size a plain integer, no C++ or framework types.
+ *
+ * What the library computes
+ * -------------------------
+ * Scaled dot-product attention softmax(Q K^T / sqrt(d)) V (Space Bunny
+ * inference-stack article, m.xxqk.cn, section 3.1), computed tile by tile with
+ * the online-softmax merge of a running maximum and normaliser ("分块稀疏注意力
+ * 与KV Cache量化：长文本推理显存优化实践", xdnf.cn, section 2.2), over a KV cache
+ * whose values are stored as grouped asymmetric integer codes (same page,
+ * section 2.4: adjacent channels form a group with its own scale and zero-point;
+ * section 3.2: group size 32) and dequantised inside the tile load (section
+ * 1.3: dequantise on read instead of a separate pass), with KV-tile skipping
+ * driven by a block mask (section 2.3).  Query head h reads KV head
+ * h / (num_q_heads / num_kv_heads) (grouped-query attention).
+ *
+ * Quantisation of one group x[0..31] (32 consecutive head_dim channels of one
+ * token of one KV head), qmax = 2^bits - 1:
+ *   lo = min(0, min x), hi = max(0, max x)
+ *   s  = least fp16 value with s * qmax >= hi - lo   (s = +0 when hi == lo)
+ *   z  = round-half-even(-lo / s)                     (exact quotient)
+ *   c  = clamp(round-half-even(x / s) + z, 0, qmax)   (exact quotient)
+ *   dequantised value: (c - z) * s  (exact in fp32)
+ *
+ * Memory layout (all buffers contiguous, owned by the caller)
+ * -------------------------------------------------------------
+ * A cache (K or V) has batch B, num_kv_heads Hkv, head_dim D (= 128 for the
+ * attention calls; any multiple of 32 for quantise/dequantise), capacity C
+ * (a multiple of 128) and per-head bit widths bits[h] in {4, 8}.
+ * RB(h) = D * bits[h] / 8 code bytes per token.  The codes of (b, h) start at
+ *     b * C * sum_h RB(h)  +  C * sum_{h' < h} RB(h').
+ *   TAQ_LAYOUT_TOKEN (required for K): token t's RB(h) bytes at t * RB(h); in
+ *     them channel c's code is byte c (int8) or nibble c % 2 (0 = low) of
+ *     byte c / 2 (int4).  scales: fp16 [B][Hkv][C][D/32]; zeros: u8, same shape.
+ *   TAQ_LAYOUT_CHANNEL (required for V): tokens in blocks of 128; block j holds
+ *     D rows of 128 * bits / 8 bytes; row d holds channel d of the block's 128
+ *     tokens: byte t % 128 (int8) or nibble (t % 128) % 2 of byte
+ *     (t % 128) / 2 (int4).  scales: fp16 [B][Hkv][D/32][C]; zeros: u8, same.
+ *   The channel layout gives the PV matrix product its key-contiguous operand
+ *   straight from memory.
+ * Q, O: fp16 bit patterns, decode [B][Hq][D], prefill [B][Hq][L][D].
+ * Skip mask: u8, 1 = compute the 128x128 tile, 0 = skip it; element
+ *   data[b*stride_b + g*stride_h + qt*n_k_tiles + kt] for KV head g (strides
+ *   may be 0 to share one mask); causality still applies inside kept tiles and
+ *   entries above the diagonal are ignored.
+ *
+ * Conventions
+ * -----------
+ * - Every call validates its host-visible arguments before launching anything
+ *   and returns a status; on failure nothing is launched and taq_last_error()
+ *   (thread-local) holds a message.  There is no fallback path: a device that
+ *   is not gfx950 gets TAQ_ERR_UNSUPPORTED.
+ * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *   default stream).  Buffers must stay alive until the stream reaches it.
+ * - The library allocates no device memory; decode scratch is the caller's
+ *   `workspace`, sized by taq_attn_decode_workspace_bytes.
+ * - Device pointers must be 16-byte aligned (TAQ_ERR_MISALIGNED otherwise).
+ * - Device-resident lengths are clamped to [0, max_seq_len] by the kernels.
+ * - softmax_scale = 0 means 1/sqrt(head_dim).
+ * - Rows with no permitted key (and prefill rows at or beyond the sequence's
+ *   length) are written as zeros.
+ */
+#ifndef TAQ_H
+#define TAQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TAQ_ABI_VERSION 1
+#define TAQ_MAX_KV_HEADS 64
+#define TAQ_TILE 128
+#define TAQ_GROUP 32
+
+typedef enum {
+  TAQ_OK = 0,
+  TAQ_ERR_INVALID_ARGUMENT = 1,
+  TAQ_ERR_UNSUPPORTED = 2,
+  TAQ_ERR_MISALIGNED = 3,
+  TAQ_ERR_WORKSPACE_TOO_SMALL = 4,
+  TAQ_ERR_HIP = 5
+} taq_status;
+
+typedef enum { TAQ_LAYOUT_TOKEN = 0, TAQ_LAYOUT_CHANNEL = 1 } taq_layout;
+
+/* One quantised cache (K or V).  `bits` is a HOST array read only during the
+ * call; codes/scales/zeros are device buffers of taq_kv_codes_bytes() bytes and
+ * taq_kv_meta_count() elements each. */
+typedef struct {
+  int32_t batch;
+  int32_t num_kv_heads;   /* 1 .. TAQ_MAX_KV_HEADS */
+  int32_t head_dim;       /* multiple of 32 */
+  int32_t group_size;     /* must be 32 */
+  int32_t capacity;       /* tokens per (batch, head); multiple of 128 */
+  int32_t layout;         /* taq_layout */
+  const uint8_t* bits;    /* host [num_kv_heads], each 4 or 8 */
+  uint8_t* codes;         /* device */
+  uint16_t* scales;       /* device, fp16 bit patterns */
+  uint8_t* zeros;         /* device */
+} taq_kv_cache;
+
+/* KV-tile skip mask over 128x128 tiles (device data). */
+typedef struct {
+  const uint8_t* data;
+  int32_t tile;           /* must be 128 */
+  int32_t n_q_tiles;      /* decode: 1 */
+  int32_t n_k_tiles;      /* >= ceil(max_seq_len / 128) */
+  int64_t stride_b;       /* elements between batch entries (0 = shared) */
+  int64_t stride_h;       /* elements between KV heads (0 = shared) */
+} taq_tile_mask;
+
+/* Thread-local text of the last non-OK status of this thread. */
+const char* taq_last_error(void);
+int taq_abi_version(void);
+
+/* TAQ_OK when `device` is a gfx950 GPU, TAQ_ERR_UNSUPPORTED otherwise. */
+taq_status taq_device_check(int device);
+
+/* Size of the codes buffer in bytes, and the number of scales (= zeros).
+ * Return 0 for an invalid descriptor. */
+size_t taq_kv_codes_bytes(const taq_kv_cache* cache);
+size_t taq_kv_meta_count(const taq_kv_cache* cache);
+
+/* Quantise fp16 x [B][Hkv][count][D] into tokens start .. start+count-1 of
+ * every (batch, head) of `cache` (section 2.4 of the KV-quantisation page).
+ * Codes, scales and zeros of other tokens are left unchanged.  Bit-exact with
+ * the definition at the top of this file.  Errors: INVALID_ARGUMENT (null
+ * pointer, start/count out of [0, capacity], bad shape), UNSUPPORTED (bits not
+ * 4/8, group_size not 32, head_dim not a multiple of 32), MISALIGNED. */
+taq_status taq_kv_quantize(const taq_kv_cache* cache, const void* x_f16,
+                           int32_t start, int32_t count, void* stream);
+
+/* Dequantise tokens start .. start+count-1 into out [B][Hkv][count][D] as
+ * fp32 (exact) and/or fp16 (round-to-nearest-even of the exact value); either
+ * output may be NULL but not both.  A checking aid for the stored format. */
+taq_status taq_kv_dequantize(const taq_kv_cache* cache, int32_t start,
+                             int32_t count, float* out_f32, void* out_f16,
+                             void* stream);
+
+/* Workspace bytes that taq_attn_decode needs for these shapes. */
+size_t taq_attn_decode_workspace_bytes(const taq_kv_cache* k_cache,
+                                       int32_t num_q_heads,
+                                       int32_t max_seq_len);
+
+/* Single-token decode: for each batch entry b and query head h, attention of
+ * q[b][h] over keys 0 .. seq_lens[b]-1 of KV head h / (Hq/Hkv) (the new
+ * token is already in the cache), skipping KV tiles the mask drops
+ * (n_q_tiles == 1).  Split over KV chunks; the partial (max, normaliser,
+ * accumulator) triples are merged in a fixed order, so results are bitwise
+ * repeatable.  k_cache must use TAQ_LAYOUT_TOKEN and v_cache
+ * TAQ_LAYOUT_CHANNEL, with equal geometry; head_dim must be 128; num_q_heads /
+ * num_kv_heads in {1, 2, 4, 8}.  seq_lens is a device int32 [B]; max_seq_len
+ * (host) bounds it and must not exceed the capacity.  Errors: as above, plus
+ * WORKSPACE_TOO_SMALL. */
+taq_status taq_attn_decode(const taq_kv_cache* k_cache,
+                           const taq_kv_cache* v_cache, const void* q_f16,
+                           int32_t num_q_heads, const int32_t* seq_lens,
+                           int32_t max_seq_len, const taq_tile_mask* mask,
+                           float softmax_scale, void* o_f16, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Causal prefill with equal query and key lengths: q/o [B][Hq][L][D] where
+ * L = max_seq_len; row i of batch b attends to keys j <= i, j < seq_lens[b],
+ * in tiles the mask keeps (NULL = dense causal).  Query-row tiles whose whole
+ * KV range is skipped cost nothing.  Same cache requirements as decode. */
+taq_status taq_attn_prefill(const taq_kv_cache* k_cache,
+                            const taq_kv_cache* v_cache, const void* q_f16,
+                            int32_t num_q_heads, const int32_t* seq_lens,
+                            int32_t max_seq_len, const taq_tile_mask* mask,
+                            float softmax_scale, void* o_f16, void* stream);
+
+/* Test hook: when `arch` is non-NULL, taq_device_check compares this string
+ * instead of the device's architecture name (NULL restores the real check). */
+void taq_debug_set_arch_override(const char* arch);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TAQ_H */

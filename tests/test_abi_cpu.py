@@ -1,0 +1,155 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, sizes buffers, and rejects bad arguments with the documented
+status before touching the device (fake, never dereferenced pointers)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import tiled_attention_quantized_amd as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, MISALIGNED, WS_SMALL, HIP = range(6)
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "taq.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(taq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = T.lib()
+    names = header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(T.EXPORTS)
+    assert L.taq_abi_version() == 1
+
+
+def cache(B=2, H=2, D=128, cap=256, bits=(8, 4), layout=0, group=32, codes=FAKE,
+          scales=FAKE, zeros=FAKE):
+    b = np.asarray(bits, dtype=np.uint8)
+    d = T._Cache(B, H, D, group, cap, layout, b.ctypes.data, codes, scales, zeros)
+    d._keep = b
+    return d
+
+
+def status_of(rc):
+    return rc, T.lib().taq_last_error().decode()
+
+
+def test_sizes():
+    L = T.lib()
+    assert L.taq_kv_codes_bytes(ctypes.byref(cache())) == 2 * 256 * (128 + 64)
+    assert L.taq_kv_meta_count(ctypes.byref(cache())) == 2 * 2 * 256 * 4
+    assert L.taq_kv_codes_bytes(ctypes.byref(cache(bits=(3, 4)))) == 0
+    # decode workspace: B * Hq * nchunk * (D + 2) * 4
+    k = cache(B=1, H=2, cap=4096, bits=(8, 8))
+    ws = L.taq_attn_decode_workspace_bytes(ctypes.byref(k), 8, 4096)
+    assert ws > 0 and ws % (130 * 4 * 8) == 0
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(bits=(3, 4)), UNSUPPORTED),
+    (dict(group=16), UNSUPPORTED),
+    (dict(D=48), UNSUPPORTED),
+    (dict(cap=200), INVALID),
+    (dict(H=0, bits=()), INVALID),
+    (dict(layout=7), INVALID),
+    (dict(codes=0), INVALID),
+    (dict(scales=FAKE + 4), MISALIGNED),
+])
+def test_quantize_rejects(kw, want):
+    d = cache(**kw)
+    rc, msg = status_of(T.lib().taq_kv_quantize(ctypes.byref(d), FAKE, 0, 4, None))
+    assert rc == want, msg
+    assert msg
+
+
+def test_quantize_range_and_pointer_checks():
+    L = T.lib()
+    d = cache()
+    assert L.taq_kv_quantize(ctypes.byref(d), FAKE, 250, 7, None) == INVALID
+    assert L.taq_kv_quantize(ctypes.byref(d), FAKE, -1, 2, None) == INVALID
+    assert L.taq_kv_quantize(ctypes.byref(d), 0, 0, 2, None) == INVALID
+    assert L.taq_kv_quantize(ctypes.byref(d), FAKE + 2, 0, 2, None) == MISALIGNED
+    assert L.taq_kv_dequantize(ctypes.byref(d), 0, 2, None, None, None) == INVALID
+    assert L.taq_kv_dequantize(ctypes.byref(d), 0, 2, FAKE + 8, None, None) == MISALIGNED
+
+
+def decode_call(k=None, v=None, hq=8, max_len=200, mask=None, ws_bytes=1 << 30,
+                q=FAKE, o=FAKE, lens=FAKE, ws=FAKE, scale=0.0):
+    k = k or cache(B=1, H=2, cap=256, bits=(8, 8), layout=0)
+    v = v or cache(B=1, H=2, cap=256, bits=(8, 8), layout=1)
+    m = ctypes.byref(mask) if mask is not None else None
+    return status_of(T.lib().taq_attn_decode(ctypes.byref(k), ctypes.byref(v), q, hq, lens,
+                                             max_len, m, scale, o, ws, ws_bytes, None))
+
+
+def prefill_call(k=None, v=None, hq=8, max_len=200, mask=None, q=FAKE, o=FAKE, lens=FAKE,
+                 scale=0.0):
+    k = k or cache(B=1, H=2, cap=256, bits=(8, 8), layout=0)
+    v = v or cache(B=1, H=2, cap=256, bits=(8, 8), layout=1)
+    m = ctypes.byref(mask) if mask is not None else None
+    return status_of(T.lib().taq_attn_prefill(ctypes.byref(k), ctypes.byref(v), q, hq, lens,
+                                              max_len, m, scale, o, None))
+
+
+@pytest.mark.parametrize("call", [decode_call, prefill_call])
+def test_attention_rejects(call):
+    assert call(hq=7)[0] == INVALID                      # Hq % Hkv != 0
+    assert call(hq=6)[0] == UNSUPPORTED                  # r = 3
+    assert call(hq=32)[0] == UNSUPPORTED                 # r = 16
+    assert call(max_len=300)[0] == INVALID               # beyond capacity
+    assert call(max_len=-1)[0] == INVALID
+    assert call(q=0)[0] == INVALID
+    assert call(o=FAKE + 2)[0] == MISALIGNED
+    assert call(scale=float("nan"))[0] == INVALID
+    kd = cache(B=1, H=2, cap=256, bits=(8, 8), layout=1)
+    assert call(k=kd)[0] == UNSUPPORTED                  # K must be token layout
+    vd = cache(B=1, H=2, cap=256, bits=(8, 8), layout=0)
+    assert call(v=vd)[0] == UNSUPPORTED                  # V must be channel layout
+    k64 = cache(B=1, H=2, D=64, cap=256, bits=(8, 8), layout=0)
+    assert call(k=k64)[0] == UNSUPPORTED                 # attention needs D = 128
+    v2 = cache(B=1, H=2, cap=384, bits=(8, 8), layout=1)
+    assert call(v=v2)[0] == INVALID                      # geometry mismatch
+    bad_tile = T._Mask(FAKE, 64, 2, 2, 0, 0)
+    assert call(mask=bad_tile)[0] == UNSUPPORTED
+    small = T._Mask(FAKE, 128, 2, 1, 0, 0)
+    assert call(mask=small)[0] == INVALID
+    nodata = T._Mask(0, 128, 2, 2, 0, 0)
+    assert call(mask=nodata)[0] == INVALID
+
+
+def test_decode_workspace_too_small():
+    assert decode_call(ws_bytes=16)[0] == WS_SMALL
+    assert decode_call(ws=0)[0] == WS_SMALL
+
+
+def test_valid_arguments_reach_the_device_check():
+    # No GPU in this container: valid arguments get past validation and stop at
+    # the device query with a HIP status, never at a fallback.
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU device node is present")
+    rc, msg = decode_call()
+    assert rc == HIP, msg
+    rc, msg = prefill_call()
+    assert rc == HIP, msg
+
+
+def test_arch_override_rejects_other_gpus():
+    L = T.lib()
+    try:
+        L.taq_debug_set_arch_override(b"gfx942:sramecc+:xnack-")
+        rc, msg = status_of(L.taq_device_check(0))
+        assert rc == UNSUPPORTED and "gfx950" in msg
+        L.taq_debug_set_arch_override(b"gfx950:sramecc+:xnack-")
+        assert L.taq_device_check(0) == OK
+    finally:
+        L.taq_debug_set_arch_override(None)

@@ -1,0 +1,145 @@
+"""GPU parity of attn_decode against the fp64 oracle (max-abs <= 2e-3), plus
+edge cases, full-size workloads on sampled heads and run-to-run determinism."""
+import numpy as np
+import pytest
+import torch
+
+import tiled_attention_quantized_amd as T
+import workloads as W
+from oracle import attention as oa
+from oracle import quant as oq
+from tests.gpu_util import (TOL, require_gpu, note, gpu_cache, max_abs, lens_tensor)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_decode(inp, mask=None, heads=None, workers=4):
+    spec, st = inp.spec, inp.structure
+    bits = st.head_bits
+    kc = gpu_cache(inp.k, bits, T.LAYOUT_TOKEN, spec.cap)
+    vc = gpu_cache(inp.v, bits, T.LAYOUT_CHANNEL, spec.cap)
+    q = torch.from_numpy(inp.q).cuda()
+    lens = lens_tensor(st.seq_lens)
+    tm = None
+    if mask is not None:
+        md = torch.from_numpy(np.ascontiguousarray(mask)).cuda()
+        tm = T.TileMask(md, 1, mask.shape[-1], stride_b=mask.shape[-1] if mask.ndim == 2 else 0)
+    out = T.attn_decode(kc, vc, q, lens, spec.max_len, mask=tm)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    # oracle: quantise with the oracle's own quantiser, then exact attention
+    okc = oq.build_cache(inp.k, bits, "token", cap=spec.cap)
+    ovc = oq.build_cache(inp.v, bits, "channel", cap=spec.cap)
+    want = oa.decode(inp.q, oq.dequantized_all(okc), oq.dequantized_all(ovc), st.seq_lens,
+                     mask=mask, heads=heads, workers=workers)
+    return got, want, (kc, vc, q, lens, tm)
+
+
+@pytest.mark.parametrize("r", [1, 2, 4, 8])
+@pytest.mark.parametrize("bits,n8", [(8, 0), (4, 0), (4, 1)])
+def test_decode_small_ragged(r, bits, n8):
+    require_gpu()
+    Hkv = 2
+    spec = W.small("decode", B=5, Hq=Hkv * r, Hkv=Hkv, ragged=(1, 700), bits=bits,
+                   n_int8_heads=n8, seed=r * 10 + bits + n8)
+    inp = W.make_inputs(spec)
+    # force edge lengths into the batch
+    inp.structure.seq_lens[:4] = [1, 31, 33, 128]
+    for b in range(4):
+        n = inp.structure.seq_lens[b]
+        inp.k[b, :, n:] = 0
+        inp.v[b, :, n:] = 0
+    note(f"decode small r={r} bits={bits} n8={n8} lens={inp.structure.seq_lens.tolist()}")
+    got, want, _ = run_decode(inp)
+    err = max_abs(got, want)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_decode_with_tile_mask(bits):
+    require_gpu()
+    spec = W.small("decode", B=3, Hq=8, Hkv=2, ragged=(300, 1000), bits=bits, seed=5)
+    inp = W.make_inputs(spec)
+    nk = spec.cap // 128
+    rng = np.random.default_rng(1)
+    mask = (rng.random((spec.B, nk)) < 0.6).astype(np.uint8)
+    mask[:, 0] = 1
+    mask[2, :] = 0          # batch entry 2 sees no key at all -> zeros
+    note(f"decode masked bits={bits}")
+    got, want, _ = run_decode(inp, mask=mask)
+    assert max_abs(got, want) <= TOL
+    assert not got[2].any()
+
+
+def test_decode_zero_length_and_uniform_v():
+    require_gpu()
+    spec = W.small("decode", B=3, Hq=4, Hkv=1, ragged=(1, 400), bits=8, seed=9)
+    inp = W.make_inputs(spec)
+    inp.structure.seq_lens[1] = 0
+    inp.k[1] = 0
+    inp.v[1] = 0
+    # uniform V for batch 0: every key carries the same value row
+    n0 = inp.structure.seq_lens[0]
+    inp.v[0, :, :n0] = inp.v[0, :, :1]
+    note("decode zero length + uniform V")
+    got, want, _ = run_decode(inp)
+    assert max_abs(got, want) <= TOL
+    assert not got[1].any()
+    vhat = oq.dequantize(*oq.quantize(inp.v[0, 0, :1], 8)).astype(np.float16).astype(np.float64)
+    # output equals that value up to one fp16 ulp
+    ulp = np.abs(np.spacing(vhat.astype(np.float16))).astype(np.float64)
+    assert np.all(np.abs(got[0] - vhat) <= ulp + 1e-12)
+
+
+def test_decode_deterministic():
+    require_gpu()
+    spec = W.small("decode", B=4, Hq=16, Hkv=4, ragged=(100, 3000), bits=4, seed=3)
+    inp = W.make_inputs(spec)
+    note("decode determinism")
+    got, want, (kc, vc, q, lens, _) = run_decode(inp)
+    for _ in range(3):
+        again = T.attn_decode(kc, vc, q, lens, spec.max_len)
+        torch.cuda.synchronize()
+        assert np.array_equal(again.cpu().numpy().view(np.uint16),
+                              got.astype(np.float16).view(np.uint16))
+
+
+def test_decode_4k_workload_full():
+    """B=1, Hq=8, Hkv=2, context 4096, int8: every output checked."""
+    require_gpu()
+    inp = W.make_inputs(W.WORKLOADS["decode_4k"])
+    note("decode_4k full")
+    got, want, _ = run_decode(inp)
+    assert max_abs(got, want) <= TOL
+
+
+@pytest.mark.parametrize("name", ["decode_ragged", "decode_128k_mixed"])
+def test_decode_full_size_sampled(name):
+    """Full-size workloads in the benchmarked launch configuration; the oracle
+    checks a sample of (batch, query head) outputs."""
+    require_gpu()
+    spec = W.WORKLOADS[name]
+    inp = W.make_inputs(spec)
+    rng = np.random.default_rng(0)
+    B, Hq = spec.B, spec.Hq
+    heads = sorted({(int(b), int(h)) for b, h in zip(rng.integers(0, B, 12), rng.integers(0, Hq, 12))}
+                   | {(0, 0), (B - 1, Hq - 1)})
+    note(f"{name} full size, sampled heads {heads}")
+    st = inp.structure
+    bits = st.head_bits
+    kc = gpu_cache(inp.k, bits, T.LAYOUT_TOKEN, spec.cap)
+    vc = gpu_cache(inp.v, bits, T.LAYOUT_CHANNEL, spec.cap)
+    q = torch.from_numpy(inp.q).cuda()
+    out = T.attn_decode(kc, vc, q, lens_tensor(st.seq_lens), spec.max_len)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    del kc, vc
+    r = spec.r
+    for b, h in heads:
+        g = h // r
+        n = int(st.seq_lens[b])
+        kh = oq.dequantize(*oq.quantize(inp.k[b, g, :n], int(bits[g])))
+        vh = oq.dequantize(*oq.quantize(inp.v[b, g, :n], int(bits[g])))
+        want = oa.decode(inp.q[b:b + 1, h:h + 1], kh[None, None], vh[None, None], [n])[0, 0]
+        err = max_abs(got[b, h], want)
+        assert err <= TOL, (b, h, err)

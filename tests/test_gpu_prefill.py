@@ -1,0 +1,146 @@
+"""GPU parity of attn_prefill against the fp64 oracle (max-abs <= 2e-3): small
+shapes checked everywhere (ragged lengths, several tiles and a ragged tail,
+masks, GQA ratios, mixed bits), full-size workloads on sampled rows, invariants
+and determinism."""
+import numpy as np
+import pytest
+import torch
+
+import tiled_attention_quantized_amd as T
+import workloads as W
+from oracle import attention as oa
+from oracle import quant as oq
+from tests.gpu_util import (TOL, require_gpu, note, gpu_cache, max_abs, lens_tensor)
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_run(inp, mask=None, lens=None):
+    spec, st = inp.spec, inp.structure
+    bits = st.head_bits
+    kc = gpu_cache(inp.k, bits, T.LAYOUT_TOKEN, spec.cap)
+    vc = gpu_cache(inp.v, bits, T.LAYOUT_CHANNEL, spec.cap)
+    q = torch.from_numpy(inp.q).cuda()
+    lt = lens_tensor(st.seq_lens if lens is None else lens)
+    tm = None
+    if mask is not None:
+        md = torch.from_numpy(np.ascontiguousarray(mask)).cuda()
+        tm = T.TileMask(md, mask.shape[-2], mask.shape[-1],
+                        stride_b=mask.shape[-2] * mask.shape[-1] if mask.ndim == 3 else 0)
+    out = T.attn_prefill(kc, vc, q, lt, mask=tm)
+    torch.cuda.synchronize()
+    return out, (kc, vc, q, lt, tm)
+
+
+def gpu_run_np(inp, mask=None, lens=None):
+    out, ctx = gpu_run(inp, mask=mask, lens=lens)
+    return out.cpu().numpy().astype(np.float64), ctx
+
+
+def oracle_run(inp, mask=None, lens=None, rows=None, heads=None, workers=4):
+    spec, st = inp.spec, inp.structure
+    bits = st.head_bits
+    okc = oq.build_cache(inp.k, bits, "token", cap=spec.cap)
+    ovc = oq.build_cache(inp.v, bits, "channel", cap=spec.cap)
+    return oa.prefill(inp.q, oq.dequantized_all(okc), oq.dequantized_all(ovc),
+                      st.seq_lens if lens is None else lens, mask=mask, rows=rows,
+                      heads=heads, workers=workers)
+
+
+@pytest.mark.parametrize("r", [1, 2, 4, 8])
+@pytest.mark.parametrize("L", [1, 77, 200, 513])
+def test_prefill_small_dense(r, L):
+    require_gpu()
+    Hkv = 2 if r < 8 else 1
+    spec = W.small("prefill", B=2, Hq=Hkv * r, Hkv=Hkv, L=L, bits=8, seed=r + L)
+    inp = W.make_inputs(spec)
+    lens = np.array([L, max(1, L // 2 + 3) if L > 1 else 1], dtype=np.int32)
+    note(f"prefill dense r={r} L={L} lens={lens.tolist()}")
+    got, _ = gpu_run_np(inp, lens=lens)
+    want = oracle_run(inp, lens=lens)
+    err = max_abs(got, want)
+    assert err <= TOL, err
+    # rows at or beyond the sequence length are zero
+    assert not got[1, :, lens[1]:].any()
+
+
+@pytest.mark.parametrize("bits,n8", [(4, 0), (4, 1), (8, 1)])
+def test_prefill_bits(bits, n8):
+    require_gpu()
+    spec = W.small("prefill", B=1, Hq=8, Hkv=2, L=384, bits=bits, n_int8_heads=n8, seed=3)
+    inp = W.make_inputs(spec)
+    note(f"prefill bits={bits} n8={n8}")
+    got, _ = gpu_run_np(inp)
+    want = oracle_run(inp)
+    assert max_abs(got, want) <= TOL
+
+
+@pytest.mark.parametrize("r", [4, 1])
+def test_prefill_masked(r):
+    require_gpu()
+    L = 640
+    spec = W.small("prefill", B=2, Hq=2 * r, Hkv=2, L=L, bits=8, seed=11)
+    inp = W.make_inputs(spec)
+    rng = np.random.default_rng(4)
+    nt = 5
+    mask = np.stack([W.skip_mask(L, 0.4, rng) for _ in range(2)])
+    mask[1, 3, 3] = 0      # a dropped diagonal: rows 384..511 of batch 1 see keys in kept tiles only
+    mask[1, 4, :] = 0      # query tile 4 of batch 1 sees nothing -> zeros
+    assert mask.shape == (2, nt, nt)
+    note(f"prefill masked r={r}")
+    got, _ = gpu_run_np(inp, mask=mask)
+    want = oracle_run(inp, mask=mask)
+    assert max_abs(got, want) <= TOL
+    assert not got[1, :, 512:].any()
+
+
+def test_prefill_uniform_v_and_determinism():
+    require_gpu()
+    spec = W.small("prefill", B=1, Hq=4, Hkv=1, L=300, bits=8, seed=21)
+    inp = W.make_inputs(spec)
+    inp.v[0, 0, :300] = inp.v[0, 0, :1]
+    note("prefill uniform V")
+    got, (kc, vc, q, lt, tm) = gpu_run_np(inp)
+    vhat = oq.dequantize(*oq.quantize(inp.v[0, 0, :1], 8)).astype(np.float16)
+    ulp = np.abs(np.spacing(vhat)).astype(np.float64)
+    assert np.all(np.abs(got[0] - vhat.astype(np.float64)) <= ulp + 1e-12)
+    for _ in range(2):
+        again = T.attn_prefill(kc, vc, q, lt)
+        torch.cuda.synchronize()
+        assert np.array_equal(again.cpu().numpy().view(np.uint16),
+                              got.astype(np.float16).view(np.uint16))
+
+
+def _sample_rows(L, rng, n=48):
+    fixed = [0, 1, 2, 3, 127, 128, 129, L // 2, L - 129, L - 128, L - 2, L - 1]
+    rows = set(int(x) for x in fixed if 0 <= x < L)
+    rows |= set(int(x) for x in rng.integers(0, L, n))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["prefill_8k", "prefill_128k_sparse"])
+def test_prefill_full_size_sampled(name):
+    """Full-size workloads in the benchmarked launch configuration; sampled
+    rows of sampled heads against the oracle."""
+    require_gpu()
+    spec = W.WORKLOADS[name]
+    inp = W.make_inputs(spec)
+    st = inp.structure
+    rng = np.random.default_rng(1)
+    note(f"{name} full size")
+    out, ctx = gpu_run(inp, mask=st.mask)
+    del ctx
+    rows = _sample_rows(spec.context, rng)
+    heads = [(0, 0), (0, 5), (0, 18), (0, 31)]
+    bits = st.head_bits
+    r = spec.r
+    for b, h in heads:
+        g = h // r
+        n = int(st.seq_lens[b])
+        kh = oq.dequantize(*oq.quantize(inp.k[b, g, :n], int(bits[g])))
+        vh = oq.dequantize(*oq.quantize(inp.v[b, g, :n], int(bits[g])))
+        want = oa.prefill(inp.q[b:b + 1, h:h + 1], kh[None, None], vh[None, None], [n],
+                          mask=st.mask, rows=rows)[0, 0]
+        got = out[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+        err = max_abs(got, want)
+        assert err <= TOL, (h, err)

@@ -1,0 +1,318 @@
+// C ABI of the library: argument validation, cache geometry and launches.
+// Every entry point checks what the host can see before anything is enqueued
+// and never substitutes another code path ("分块稀疏注意力与KV Cache量化：长文本
+// 推理显存优化实践", xdnf.cn, section 4.3, describes what a silent fallback costs).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "taq_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+std::mutex g_arch_mu;
+std::string g_arch_override;
+bool g_arch_override_set = false;
+
+taq_status fail(taq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+taq_status hip_fail(hipError_t e, const char* what) {
+  return fail(TAQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+taq_status check_cache(const taq_kv_cache* c, const char* name, int need_layout,
+                       bool attention) {
+  if (!c) return fail(TAQ_ERR_INVALID_ARGUMENT, "%s: null cache descriptor", name);
+  if (c->batch < 1) return fail(TAQ_ERR_INVALID_ARGUMENT, "%s: batch must be >= 1", name);
+  if (c->num_kv_heads < 1 || c->num_kv_heads > TAQ_MAX_KV_HEADS)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "%s: num_kv_heads must be in [1, %d]", name,
+                TAQ_MAX_KV_HEADS);
+  if (c->group_size != TAQ_GROUP)
+    return fail(TAQ_ERR_UNSUPPORTED, "%s: group_size must be 32", name);
+  if (c->head_dim <= 0 || c->head_dim % TAQ_GROUP)
+    return fail(TAQ_ERR_UNSUPPORTED, "%s: head_dim must be a positive multiple of 32", name);
+  if (attention && c->head_dim != 128)
+    return fail(TAQ_ERR_UNSUPPORTED, "%s: attention kernels need head_dim 128", name);
+  if (c->capacity <= 0 || c->capacity % TAQ_TILE)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "%s: capacity must be a positive multiple of 128",
+                name);
+  if (c->layout != TAQ_LAYOUT_TOKEN && c->layout != TAQ_LAYOUT_CHANNEL)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "%s: unknown layout %d", name, c->layout);
+  if (need_layout >= 0 && c->layout != need_layout)
+    return fail(TAQ_ERR_UNSUPPORTED, "%s: layout must be %s", name,
+                need_layout == TAQ_LAYOUT_TOKEN ? "TAQ_LAYOUT_TOKEN" : "TAQ_LAYOUT_CHANNEL");
+  if (!c->bits) return fail(TAQ_ERR_INVALID_ARGUMENT, "%s: null bits array", name);
+  for (int h = 0; h < c->num_kv_heads; ++h)
+    if (c->bits[h] != 4 && c->bits[h] != 8)
+      return fail(TAQ_ERR_UNSUPPORTED, "%s: bits[%d] = %d (must be 4 or 8)", name, h,
+                  (int)c->bits[h]);
+  if (!c->codes || !c->scales || !c->zeros)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "%s: null device buffer", name);
+  if (!aligned16(c->codes) || !aligned16(c->scales) || !aligned16(c->zeros))
+    return fail(TAQ_ERR_MISALIGNED, "%s: device buffers must be 16-byte aligned", name);
+  return TAQ_OK;
+}
+
+taq::CacheGeom geom_of(const taq_kv_cache* c) {
+  taq::CacheGeom g;
+  std::memset(&g, 0, sizeof(g));
+  g.codes = c->codes;
+  g.scales = c->scales;
+  g.zeros = c->zeros;
+  int64_t acc = 0;
+  for (int h = 0; h < c->num_kv_heads; ++h) {
+    g.hoff[h] = acc;
+    acc += (int64_t)c->capacity * c->head_dim * c->bits[h] / 8;
+    if (c->bits[h] == 8) g.is8 |= 1ull << h;
+  }
+  g.bstride = acc;
+  g.B = c->batch;
+  g.H = c->num_kv_heads;
+  g.D = c->head_dim;
+  g.cap = c->capacity;
+  g.layout = c->layout;
+  return g;
+}
+
+taq_status device_ok() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  return taq_device_check(dev);
+}
+
+taq_status check_mask(const taq_tile_mask* m, int need_q, int need_k) {
+  if (!m) return TAQ_OK;
+  if (!m->data) return fail(TAQ_ERR_INVALID_ARGUMENT, "mask: null data");
+  if (m->tile != TAQ_TILE) return fail(TAQ_ERR_UNSUPPORTED, "mask: tile must be 128");
+  if (m->n_q_tiles < need_q || m->n_k_tiles < need_k)
+    return fail(TAQ_ERR_INVALID_ARGUMENT,
+                "mask: needs at least %d x %d tiles, got %d x %d", need_q, need_k,
+                m->n_q_tiles, m->n_k_tiles);
+  if (m->stride_b < 0 || m->stride_h < 0)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "mask: negative stride");
+  return TAQ_OK;
+}
+
+taq_status check_pair(const taq_kv_cache* k, const taq_kv_cache* v, int32_t hq,
+                      int32_t max_len) {
+  taq_status st = check_cache(k, "k_cache", TAQ_LAYOUT_TOKEN, true);
+  if (st) return st;
+  st = check_cache(v, "v_cache", TAQ_LAYOUT_CHANNEL, true);
+  if (st) return st;
+  if (k->batch != v->batch || k->num_kv_heads != v->num_kv_heads ||
+      k->head_dim != v->head_dim || k->capacity != v->capacity)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "k_cache and v_cache geometry differ");
+  if (hq < 1 || hq % k->num_kv_heads)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "num_q_heads (%d) must be a positive multiple of "
+                "num_kv_heads (%d)", hq, k->num_kv_heads);
+  const int r = hq / k->num_kv_heads;
+  if (r != 1 && r != 2 && r != 4 && r != 8)
+    return fail(TAQ_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads = %d (supported: 1, 2, 4, 8)", r);
+  if (max_len < 0 || max_len > k->capacity)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "max_seq_len %d outside [0, capacity %d]", max_len,
+                k->capacity);
+  return TAQ_OK;
+}
+
+float scale_log2_of(float softmax_scale, int D) {
+  const float s = softmax_scale == 0.f ? 1.f / std::sqrt((float)D) : softmax_scale;
+  return s * 1.4426950408889634f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* taq_last_error(void) { return g_err.c_str(); }
+
+int taq_abi_version(void) { return TAQ_ABI_VERSION; }
+
+void taq_debug_set_arch_override(const char* arch) {
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  g_arch_override_set = arch != nullptr;
+  g_arch_override = arch ? arch : "";
+}
+
+taq_status taq_device_check(int device) {
+  std::string arch;
+  {
+    std::lock_guard<std::mutex> lk(g_arch_mu);
+    if (g_arch_override_set) arch = g_arch_override;
+  }
+  if (arch.empty()) {
+    hipDeviceProp_t p;
+    hipError_t e = hipGetDeviceProperties(&p, device);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    arch = p.gcnArchName;
+  }
+  if (arch.compare(0, 6, "gfx950") != 0)
+    return fail(TAQ_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950 only",
+                device, arch.c_str());
+  return TAQ_OK;
+}
+
+size_t taq_kv_codes_bytes(const taq_kv_cache* c) {
+  if (check_cache(c, "cache", -1, false)) return 0;
+  size_t per = 0;
+  for (int h = 0; h < c->num_kv_heads; ++h)
+    per += (size_t)c->capacity * c->head_dim * c->bits[h] / 8;
+  return per * (size_t)c->batch;
+}
+
+size_t taq_kv_meta_count(const taq_kv_cache* c) {
+  if (check_cache(c, "cache", -1, false)) return 0;
+  return (size_t)c->batch * c->num_kv_heads * c->capacity * (c->head_dim / TAQ_GROUP);
+}
+
+taq_status taq_kv_quantize(const taq_kv_cache* c, const void* x, int32_t start,
+                           int32_t count, void* stream) {
+  taq_status st = check_cache(c, "cache", -1, false);
+  if (st) return st;
+  if (!x) return fail(TAQ_ERR_INVALID_ARGUMENT, "x: null");
+  if (!aligned16(x)) return fail(TAQ_ERR_MISALIGNED, "x must be 16-byte aligned");
+  if (start < 0 || count < 0 || (int64_t)start + count > c->capacity)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "tokens [%d, %d + %d) outside capacity %d", start,
+                start, count, c->capacity);
+  st = device_ok();
+  if (st) return st;
+  taq::QuantArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.c = geom_of(c);
+  a.x = static_cast<const uint16_t*>(x);
+  a.start = start;
+  a.count = count;
+  hipError_t e = taq::launch_kv_quantize(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TAQ_OK : hip_fail(e, "kv_quantize launch");
+}
+
+taq_status taq_kv_dequantize(const taq_kv_cache* c, int32_t start, int32_t count,
+                             float* out32, void* out16, void* stream) {
+  taq_status st = check_cache(c, "cache", -1, false);
+  if (st) return st;
+  if (!out32 && !out16) return fail(TAQ_ERR_INVALID_ARGUMENT, "both outputs are null");
+  if ((out32 && !aligned16(out32)) || (out16 && !aligned16(out16)))
+    return fail(TAQ_ERR_MISALIGNED, "outputs must be 16-byte aligned");
+  if (start < 0 || count < 0 || (int64_t)start + count > c->capacity)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "tokens [%d, %d + %d) outside capacity %d", start,
+                start, count, c->capacity);
+  st = device_ok();
+  if (st) return st;
+  taq::QuantArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.c = geom_of(c);
+  a.start = start;
+  a.count = count;
+  a.out32 = out32;
+  a.out16 = static_cast<uint16_t*>(out16);
+  hipError_t e = taq::launch_kv_dequantize(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TAQ_OK : hip_fail(e, "kv_dequantize launch");
+}
+
+size_t taq_attn_decode_workspace_bytes(const taq_kv_cache* k, int32_t hq, int32_t max_len) {
+  if (!k || k->batch < 1 || k->num_kv_heads < 1 || hq < 1 || max_len < 0) return 0;
+  const int chunk = taq::decode_chunk_tokens(k->batch, k->num_kv_heads, max_len);
+  const int64_t nchunk = max_len > 0 ? (max_len + chunk - 1) / chunk : 1;
+  return (size_t)k->batch * hq * nchunk * (128 + 2) * sizeof(float);
+}
+
+taq_status taq_attn_decode(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
+                           int32_t hq, const int32_t* lens, int32_t max_len,
+                           const taq_tile_mask* mask, float softmax_scale, void* o,
+                           void* ws, size_t ws_bytes, void* stream) {
+  taq_status st = check_pair(k, v, hq, max_len);
+  if (st) return st;
+  if (!q || !o || !lens) return fail(TAQ_ERR_INVALID_ARGUMENT, "null q, o or seq_lens");
+  if (!aligned16(q) || !aligned16(o) || !aligned16(lens))
+    return fail(TAQ_ERR_MISALIGNED, "q, o and seq_lens must be 16-byte aligned");
+  if (!std::isfinite(softmax_scale))
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  st = check_mask(mask, 1, (max_len + TAQ_TILE - 1) / TAQ_TILE);
+  if (st) return st;
+  const size_t need = taq_attn_decode_workspace_bytes(k, hq, max_len);
+  if (!ws || ws_bytes < need)
+    return fail(TAQ_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(TAQ_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  st = device_ok();
+  if (st) return st;
+  taq::DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k = geom_of(k);
+  a.v = geom_of(v);
+  a.q = static_cast<const uint16_t*>(q);
+  a.o = static_cast<uint16_t*>(o);
+  a.lens = lens;
+  if (mask) {
+    a.mask = mask->data;
+    a.mask_sb = mask->stride_b;
+    a.mask_sh = mask->stride_h;
+    a.mask_nk = mask->n_k_tiles;
+  }
+  a.ws = static_cast<float*>(ws);
+  a.Hq = hq;
+  a.r = hq / k->num_kv_heads;
+  a.max_len = max_len;
+  a.chunk = taq::decode_chunk_tokens(k->batch, k->num_kv_heads, max_len);
+  a.nchunk = max_len > 0 ? (max_len + a.chunk - 1) / a.chunk : 1;
+  a.scale_log2 = scale_log2_of(softmax_scale, 128);
+  hipError_t e = taq::launch_attn_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TAQ_OK : hip_fail(e, "attn_decode launch");
+}
+
+taq_status taq_attn_prefill(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
+                            int32_t hq, const int32_t* lens, int32_t max_len,
+                            const taq_tile_mask* mask, float softmax_scale, void* o,
+                            void* stream) {
+  taq_status st = check_pair(k, v, hq, max_len);
+  if (st) return st;
+  if (!q || !o || !lens) return fail(TAQ_ERR_INVALID_ARGUMENT, "null q, o or seq_lens");
+  if (!aligned16(q) || !aligned16(o) || !aligned16(lens))
+    return fail(TAQ_ERR_MISALIGNED, "q, o and seq_lens must be 16-byte aligned");
+  if (!std::isfinite(softmax_scale))
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  const int nt = (max_len + TAQ_TILE - 1) / TAQ_TILE;
+  st = check_mask(mask, nt, nt);
+  if (st) return st;
+  st = device_ok();
+  if (st) return st;
+  if (max_len == 0) return TAQ_OK;
+  taq::PrefillArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k = geom_of(k);
+  a.v = geom_of(v);
+  a.q = static_cast<const uint16_t*>(q);
+  a.o = static_cast<uint16_t*>(o);
+  a.lens = lens;
+  if (mask) {
+    a.mask = mask->data;
+    a.mask_sb = mask->stride_b;
+    a.mask_sh = mask->stride_h;
+    a.mask_nq = mask->n_q_tiles;
+    a.mask_nk = mask->n_k_tiles;
+  }
+  a.Hq = hq;
+  a.r = hq / k->num_kv_heads;
+  a.L = max_len;
+  const int bq = 256 / a.r;
+  a.n_qblk = (max_len + bq - 1) / bq;
+  a.scale_log2 = scale_log2_of(softmax_scale, 128);
+  hipError_t e = taq::launch_attn_prefill(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TAQ_OK : hip_fail(e, "attn_prefill launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Device helpers for gfx950 (CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace taq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ _Float16 bits_to_half(uint16_t b) {
+  return __builtin_bit_cast(_Float16, b);
+}
+__device__ __forceinline__ uint16_t half_to_bits(_Float16 h) {
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ half2v u32_to_h2(uint32_t u) {
+  return __builtin_bit_cast(half2v, u);
+}
+__device__ __forceinline__ uint32_t h2_to_u32(half2v h) {
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// v_perm_b32: byte i of the result is byte sel_i of the 8-byte value
+// {hi = a, lo = b} (selector 0..3 -> b, 4..7 -> a, 12 -> 0x00).
+__device__ __forceinline__ uint32_t perm_b32(uint32_t a, uint32_t b, uint32_t sel) {
+  return __builtin_amdgcn_perm(a, b, sel);
+}
+
+// Two unsigned bytes -> half2 (1024 + c0, 1024 + c1); exact.  `w` holds four
+// bytes; hi_pair selects bytes {2,3} instead of {0,1}.
+__device__ __forceinline__ uint32_t bytes_to_biased_h2(uint32_t w, bool hi_pair) {
+  return perm_b32(0x64646464u, w, hi_pair ? 0x04030402u : 0x04010400u);
+}
+
+// Two nibbles at bit offsets 4k and 16 + 4k of w -> half2 (1024 + n, 1024 + n').
+__device__ __forceinline__ uint32_t nibbles_to_biased_h2(uint32_t w, int k) {
+  return ((w >> (4 * k)) & 0x000F000Fu) | 0x64006400u;
+}
+
+// half2 (-(1024 + z), -(1024 + z)) for one byte z (bits 0..7 of zb).
+__device__ __forceinline__ uint32_t neg_biased_zero_h2(uint32_t zb) {
+  return (zb & 0xFFu) * 0x00010001u | 0xE400E400u;
+}
+
+// DPP moves inside rows of 16 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+// quad_perm [1,0,3,2], [2,3,0,1]; row_half_mirror; row_mirror.
+constexpr int DPP_QXOR1 = 0xB1;
+constexpr int DPP_QXOR2 = 0x4E;
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+
+// Max / sum over each row of 16 lanes; every lane gets its row's result.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<DPP_QXOR1>(x));
+  x = fmaxf(x, dpp_f<DPP_QXOR2>(x));
+  x = fmaxf(x, dpp_f<DPP_HALF_MIRROR>(x));
+  x = fmaxf(x, dpp_f<DPP_MIRROR>(x));
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<DPP_QXOR1>(x);
+  x += dpp_f<DPP_QXOR2>(x);
+  x += dpp_f<DPP_HALF_MIRROR>(x);
+  x += dpp_f<DPP_MIRROR>(x);
+  return x;
+}
+
+// Read a 32-bit value from lane `src` (any lane of the wave).
+__device__ __forceinline__ uint32_t lane_read(uint32_t v, int src) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
+}
+__device__ __forceinline__ float lane_read_f(float v, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x4 mfma16x16x32(half8 a, half8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x16(half8 a, half8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half8 u4_to_h8(u32x4 v) { return __builtin_bit_cast(half8, v); }
+
+}  // namespace taq

@@ -1,0 +1,283 @@
+// Grouped asymmetric KV quantisation and dequantisation kernels.
+//
+// Method: "分块稀疏注意力与KV Cache量化：长文本推理显存优化实践" (xdnf.cn),
+// section 2.4 -- adjacent channels form a group with its own scale and
+// zero-point -- with the group size 32 of section 3.2.  The rounding rules
+// (range widened to contain 0, scale rounded up to fp16, zero-point and codes
+// rounded half to even on the exact quotients) are stated in include/taq.h.
+//
+// Exactness: an fp16 value is an integer multiple of 2^-24 below 2^41 in those
+// units, so every quantity of one group is handled as a 64-bit integer count
+// of 2^-24; each rounding is then an integer division with its remainder, and
+// no floating-point quotient ever decides a tie.
+#include "taq_internal.h"
+#include "device_common.h"
+
+namespace taq {
+namespace {
+
+// Value of an fp16 bit pattern in units of 2^-24 (finite inputs only).
+__device__ __forceinline__ int64_t f16_units(uint32_t h) {
+  const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
+  const int64_t mag = e == 0 ? (int64_t)m : ((int64_t)(1024u + m) << (e - 1));
+  return (h & 0x8000u) ? -mag : mag;
+}
+
+// round-half-even(a / s) for a >= 0, s > 0.
+__device__ __forceinline__ uint64_t rne_div(uint64_t a, uint64_t s) {
+  uint64_t q = a / s;
+  const uint64_t r = a - q * s;
+  if (2 * r > s || (2 * r == s && (q & 1))) ++q;
+  return q;
+}
+
+// Least fp16 value >= m (m >= 1, in units of 2^-24); returns it in units and
+// as an fp16 bit pattern.
+__device__ __forceinline__ uint64_t fp16_ceil(uint64_t m, uint32_t& bits) {
+  uint64_t s = m;
+  if (m >= 2048) {
+    const int e = 63 - __clzll(m);
+    const uint64_t step = 1ull << (e - 10);
+    s = (m + step - 1) & ~(step - 1);
+  }
+  if (s < 1024) {
+    bits = (uint32_t)s;
+  } else {
+    const int e = 63 - __clzll(s);
+    const uint64_t mant = s >> (e - 10);
+    bits = ((uint32_t)(e - 9) << 10) | (uint32_t)(mant - 1024);
+  }
+  return s;
+}
+
+struct GroupQ {
+  uint8_t c[32];
+  uint32_t scale_bits;
+  uint32_t zero;
+};
+
+// Quantise the 32 fp16 values at p (16-byte aligned).
+__device__ __forceinline__ void quantize_group(const uint16_t* p, int bits,
+                                               GroupQ& out) {
+  uint32_t w[16];
+  const uint4* p4 = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = p4[i];
+    w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  }
+  int64_t x[32];
+  int64_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    x[i] = f16_units(h);
+    lo = x[i] < lo ? x[i] : lo;
+    hi = x[i] > hi ? x[i] : hi;
+  }
+  const int64_t qmax = (1 << bits) - 1;
+  const uint64_t span = (uint64_t)(hi - lo);
+  if (span == 0) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) out.c[i] = 0;
+    out.scale_bits = 0;
+    out.zero = 0;
+    return;
+  }
+  uint32_t sb;
+  const uint64_t s = fp16_ceil((span + qmax - 1) / qmax, sb);
+  const int64_t z = (int64_t)rne_div((uint64_t)(-lo), s);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint64_t a = (uint64_t)(x[i] < 0 ? -x[i] : x[i]);
+    const int64_t q = (int64_t)rne_div(a, s);
+    int64_t c = (x[i] < 0 ? -q : q) + z;
+    c = c < 0 ? 0 : (c > qmax ? qmax : c);
+    out.c[i] = (uint8_t)c;
+  }
+  out.scale_bits = sb;
+  out.zero = (uint32_t)z;
+}
+
+__device__ __forceinline__ int head_bits(const CacheGeom& g, int h) {
+  return ((g.is8 >> h) & 1ull) ? 8 : 4;
+}
+
+// Token layout: one thread per (b, h, token, group).
+__global__ void __launch_bounds__(256)
+quantize_token_kernel(QuantArgs a) {
+  const CacheGeom& g = a.c;
+  const int G = g.D / 32;
+  const int64_t total = (int64_t)g.B * g.H * a.count * G;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= total) return;
+  const int gi = (int)(id % G);
+  int64_t rest = id / G;
+  const int t = (int)(rest % a.count);
+  rest /= a.count;
+  const int h = (int)(rest % g.H);
+  const int b = (int)(rest / g.H);
+  const int bits = head_bits(g, h);
+  GroupQ q;
+  quantize_group(a.x + ((((int64_t)b * g.H + h) * a.count + t) * g.D + 32 * gi),
+                 bits, q);
+  const int T = a.start + t;
+  uint8_t* row = g.codes + (int64_t)b * g.bstride + g.hoff[h] +
+                 (int64_t)T * (g.D * bits / 8) + gi * 4 * bits;
+  if (bits == 8) {
+    uint32_t wv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      wv[i] = q.c[4 * i] | (q.c[4 * i + 1] << 8) | (q.c[4 * i + 2] << 16) |
+              ((uint32_t)q.c[4 * i + 3] << 24);
+    uint4* d = reinterpret_cast<uint4*>(row);
+    d[0] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+    d[1] = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+  } else {
+    uint32_t wv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v |= (uint32_t)q.c[8 * i + j] << (4 * j);
+      wv[i] = v;
+    }
+    *reinterpret_cast<uint4*>(row) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  }
+  const int64_t mi = (((int64_t)b * g.H + h) * g.cap + T) * G + gi;
+  g.scales[mi] = (uint16_t)q.scale_bits;
+  g.zeros[mi] = (uint8_t)q.zero;
+}
+
+// Channel layout: one thread per (b, h, group, token pair {2p, 2p+1}); both
+// tokens of a pair share their int4 bytes, so one thread owns them.
+__global__ void __launch_bounds__(256)
+quantize_channel_kernel(QuantArgs a, int p0, int npairs) {
+  const CacheGeom& g = a.c;
+  const int G = g.D / 32;
+  const int64_t total = (int64_t)g.B * g.H * G * npairs;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= total) return;
+  const int p = p0 + (int)(id % npairs);
+  int64_t rest = id / npairs;
+  const int gi = (int)(rest % G);
+  rest /= G;
+  const int h = (int)(rest % g.H);
+  const int b = (int)(rest / g.H);
+  const int bits = head_bits(g, h);
+  const int T0 = 2 * p;
+  const bool in0 = T0 >= a.start && T0 < a.start + a.count;
+  const bool in1 = T0 + 1 >= a.start && T0 + 1 < a.start + a.count;
+  GroupQ q0, q1;
+  const int64_t xbase = ((int64_t)b * g.H + h) * a.count;
+  if (in0) quantize_group(a.x + ((xbase + T0 - a.start) * g.D + 32 * gi), bits, q0);
+  if (in1) quantize_group(a.x + ((xbase + T0 + 1 - a.start) * g.D + 32 * gi), bits, q1);
+  const int rowb = 16 * bits;  // bytes per channel row of a 128-token block
+  uint8_t* blk = g.codes + (int64_t)b * g.bstride + g.hoff[h] +
+                 (int64_t)(T0 / 128) * g.D * rowb;
+  const int tt = T0 % 128;
+#pragma unroll 4
+  for (int i = 0; i < 32; ++i) {
+    uint8_t* row = blk + (int64_t)(32 * gi + i) * rowb;
+    if (bits == 8) {
+      if (in0 && in1) {
+        *reinterpret_cast<uint16_t*>(row + tt) = (uint16_t)(q0.c[i] | (q1.c[i] << 8));
+      } else if (in0) {
+        row[tt] = q0.c[i];
+      } else if (in1) {
+        row[tt + 1] = q1.c[i];
+      }
+    } else {
+      uint8_t* bp = row + tt / 2;
+      if (in0 && in1) {
+        *bp = (uint8_t)(q0.c[i] | (q1.c[i] << 4));
+      } else if (in0) {
+        *bp = (uint8_t)((*bp & 0xF0) | q0.c[i]);
+      } else if (in1) {
+        *bp = (uint8_t)((*bp & 0x0F) | (q1.c[i] << 4));
+      }
+    }
+  }
+  const int64_t mrow = (((int64_t)b * g.H + h) * G + gi) * g.cap;
+  if (in0) {
+    g.scales[mrow + T0] = (uint16_t)q0.scale_bits;
+    g.zeros[mrow + T0] = (uint8_t)q0.zero;
+  }
+  if (in1) {
+    g.scales[mrow + T0 + 1] = (uint16_t)q1.scale_bits;
+    g.zeros[mrow + T0 + 1] = (uint8_t)q1.zero;
+  }
+}
+
+// One thread per (b, h, token, group).
+__global__ void __launch_bounds__(256)
+dequantize_kernel(QuantArgs a) {
+  const CacheGeom& g = a.c;
+  const int G = g.D / 32;
+  const int64_t total = (int64_t)g.B * g.H * a.count * G;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= total) return;
+  const int gi = (int)(id % G);
+  int64_t rest = id / G;
+  const int t = (int)(rest % a.count);
+  rest /= a.count;
+  const int h = (int)(rest % g.H);
+  const int b = (int)(rest / g.H);
+  const int bits = head_bits(g, h);
+  const int T = a.start + t;
+  const uint8_t* base = g.codes + (int64_t)b * g.bstride + g.hoff[h];
+  int64_t mi;
+  if (g.layout == TAQ_LAYOUT_TOKEN)
+    mi = (((int64_t)b * g.H + h) * g.cap + T) * G + gi;
+  else
+    mi = (((int64_t)b * g.H + h) * G + gi) * g.cap + T;
+  const float s = (float)bits_to_half((uint16_t)g.scales[mi]);
+  const int z = g.zeros[mi];
+  const int64_t oi = (((int64_t)b * g.H + h) * a.count + t) * g.D + 32 * gi;
+  for (int i = 0; i < 32; ++i) {
+    const int d = 32 * gi + i;
+    int c;
+    if (g.layout == TAQ_LAYOUT_TOKEN) {
+      const uint8_t* row = base + (int64_t)T * (g.D * bits / 8);
+      c = bits == 8 ? row[d] : ((row[d / 2] >> (4 * (d & 1))) & 15);
+    } else {
+      const uint8_t* row = base + ((int64_t)(T / 128) * g.D + d) * (16 * bits);
+      const int tt = T % 128;
+      c = bits == 8 ? row[tt] : ((row[tt / 2] >> (4 * (tt & 1))) & 15);
+    }
+    const float v = (float)(c - z) * s;   // exact: <= 19 significant bits
+    if (a.out32) a.out32[oi + i] = v;
+    if (a.out16) a.out16[oi + i] = half_to_bits((_Float16)v);
+  }
+}
+
+inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+hipError_t launch_kv_quantize(const QuantArgs& a, hipStream_t s) {
+  const int G = a.c.D / 32;
+  if (a.count == 0) return hipSuccess;
+  if (a.c.layout == TAQ_LAYOUT_TOKEN) {
+    const int64_t n = (int64_t)a.c.B * a.c.H * a.count * G;
+    hipLaunchKernelGGL(quantize_token_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, a);
+  } else {
+    const int p0 = a.start / 2;
+    const int p1 = (a.start + a.count - 1) / 2;
+    const int np = p1 - p0 + 1;
+    const int64_t n = (int64_t)a.c.B * a.c.H * G * np;
+    hipLaunchKernelGGL(quantize_channel_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s,
+                       a, p0, np);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_dequantize(const QuantArgs& a, hipStream_t s) {
+  const int G = a.c.D / 32;
+  if (a.count == 0) return hipSuccess;
+  const int64_t n = (int64_t)a.c.B * a.c.H * a.count * G;
+  hipLaunchKernelGGL(dequantize_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace taq

@@ -1,0 +1,64 @@
+// Internal declarations shared by the host API and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/taq.h"
+
+namespace taq {
+
+// Geometry of one cache as the kernels see it: per-head code offsets inside a
+// batch entry and a bitmask of the 8-bit heads.
+struct CacheGeom {
+  uint8_t* codes;
+  uint16_t* scales;
+  uint8_t* zeros;
+  int64_t bstride;                      // code bytes per batch entry
+  int64_t hoff[TAQ_MAX_KV_HEADS];       // code byte offset of each head
+  uint64_t is8;                         // bit h set: head h stores int8 codes
+  int32_t B, H, D, cap, layout;
+};
+
+struct QuantArgs {
+  CacheGeom c;
+  const uint16_t* x;     // fp16 [B][H][count][D]
+  int32_t start, count;
+  float* out32;          // dequantise outputs (either may be null)
+  uint16_t* out16;
+};
+
+struct DecodeArgs {
+  CacheGeom k, v;
+  const uint16_t* q;     // [B][Hq][D]
+  uint16_t* o;           // [B][Hq][D]
+  const int32_t* lens;   // [B]
+  const uint8_t* mask;   // null = none
+  int64_t mask_sb, mask_sh;
+  int32_t mask_nk;
+  float* ws;             // partials [B][Hq][nchunk][D + 2]
+  int32_t Hq, r, max_len, chunk, nchunk;
+  float scale_log2;      // softmax scale * log2(e)
+};
+
+struct PrefillArgs {
+  CacheGeom k, v;
+  const uint16_t* q;     // [B][Hq][L][D]
+  uint16_t* o;
+  const int32_t* lens;
+  const uint8_t* mask;
+  int64_t mask_sb, mask_sh;
+  int32_t mask_nq, mask_nk;
+  int32_t Hq, r, L;
+  int32_t n_qblk;        // query blocks per (b, kv head)
+  float scale_log2;
+};
+
+hipError_t launch_kv_quantize(const QuantArgs& a, hipStream_t s);
+hipError_t launch_kv_dequantize(const QuantArgs& a, hipStream_t s);
+hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t s);
+
+// Decode split geometry chosen on the host (used for workspace sizing too).
+int decode_chunk_tokens(int B, int Hkv, int max_len);
+
+}  // namespace taq
