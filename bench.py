@@ -1,0 +1,227 @@
+"""Benchmark: tiled causal attention over a grouped-quantized KV cache on one
+MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+One step = the whole hot path over one batch of the causal-prefill workload
+(B=1, Hq=32, Hkv=8, head_dim 128, L=8192, int8 K/V, group 32): kv_quantize of
+K and V (8192 tokens each), then attn_prefill.  `value` is the algorithmic
+prefill throughput of the whole step: 4 * D * Hq * L(L+1)/2 flops divided by the
+step time.  Inputs are generated once (seeded) and resident in HBM before the
+timed region.
+
+The JSON line also carries:
+  roofline      the prefill kernel's own rate (HIP events around the launch, on
+                the stream it runs on) against dense fp16 MFMA peak;
+  decode        the long-context decode workload (B=8, Hq=32, Hkv=8, 131072
+                tokens, 2 int8 + 6 int4 KV heads): KV GB/s against HBM peak;
+  cpu_baseline  the fp64 oracle on a bounded sample of the prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_F16_PEAK_TFLOPS = 2500.0     # MI355X dense fp16 MFMA, published
+HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, published
+METRIC = "decode KV GB/s & % HBM peak; prefill TFLOP/s & % MFMA peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_caches(T, inp, torch):
+    spec, bits = inp.spec, inp.structure.head_bits
+    k = T.KVCache(spec.B, spec.Hkv, spec.D, spec.cap, bits, T.LAYOUT_TOKEN)
+    v = T.KVCache(spec.B, spec.Hkv, spec.D, spec.cap, bits, T.LAYOUT_CHANNEL)
+    return k, v
+
+
+def bench_prefill(args, torch, T, W, A):
+    spec = W.WORKLOADS["prefill_8k"]
+    log(f"generating {spec.name}")
+    inp = W.make_inputs(spec)
+    k, v = make_caches(T, inp, torch)
+    xk = torch.from_numpy(inp.k).cuda()
+    xv = torch.from_numpy(inp.v).cuda()
+    q = torch.from_numpy(inp.q).cuda()
+    out = torch.empty_like(q)
+    lens = torch.tensor(inp.structure.seq_lens, device="cuda")
+    flops = A.prefill_flops(spec.Hq, spec.D, inp.structure.seq_lens)
+    stream = torch.cuda.current_stream()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i=None):
+        T.kv_quantize(k, xk, 0)
+        T.kv_quantize(v, xv, 0)
+        if i is not None:
+            ev[i][0].record(stream)
+        T.attn_prefill(k, v, q, lens, out=out)
+        if i is not None:
+            ev[i][1].record(stream)
+
+    log("warmup")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    tflops_step = flops / dt / 1e12
+    tflops_kern = flops / (kern_ms * 1e-3) / 1e12
+    log(f"prefill: step {dt * 1e3:.3f} ms ({tflops_step:.1f} TFLOP/s), kernel {kern_ms:.3f} ms "
+        f"({tflops_kern:.1f} TFLOP/s)")
+    return spec, inp, flops, dt, kern_ms
+
+
+def bench_decode(args, torch, T, W, A):
+    spec = W.WORKLOADS["decode_128k_mixed"]
+    log(f"generating {spec.name}")
+    inp = W.make_inputs(spec)
+    k, v = make_caches(T, inp, torch)
+    T.kv_quantize(k, torch.from_numpy(inp.k).cuda(), 0)
+    T.kv_quantize(v, torch.from_numpy(inp.v).cuda(), 0)
+    q = torch.from_numpy(inp.q).cuda()
+    out = torch.empty_like(q)
+    lens = torch.tensor(inp.structure.seq_lens, device="cuda")
+    ws = torch.empty(T.decode_workspace_bytes(k, spec.Hq, spec.max_len), dtype=torch.uint8,
+                     device="cuda")
+    nbytes = A.decode_bytes(spec.B, spec.Hq, spec.D, inp.structure.seq_lens,
+                            inp.structure.head_bits)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        T.attn_decode(k, v, q, lens, spec.max_len, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    iters = max(args.steps, 10)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record(stream)
+        T.attn_decode(k, v, q, lens, spec.max_len, out=out, workspace=ws)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    med = float(np.median(ms))
+    gbs = nbytes / (med * 1e-3) / 1e9
+    log(f"decode: median {med * 1e3:.1f} us, p10 {np.percentile(ms, 10) * 1e3:.1f}, "
+        f"p90 {np.percentile(ms, 90) * 1e3:.1f}; {gbs:.0f} GB/s")
+    del k, v, q, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": spec.name, "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv,
+            "head_dim": spec.D, "context": spec.context,
+            "kv_bits": inp.structure.head_bits.tolist(),
+            "bytes_per_call": int(nbytes), "median_us": round(med * 1e3, 2),
+            "p10_us": round(float(np.percentile(ms, 10)) * 1e3, 2),
+            "p90_us": round(float(np.percentile(ms, 90)) * 1e3, 2),
+            "value": round(gbs, 1), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None}}
+
+
+def cpu_baseline(inp, A, W):
+    """The oracle as it stands on a bounded sample: 8 of the 32 query heads
+    (the 2 KV groups 0 and 1), all rows, process pool over heads."""
+    from oracle import attention as oa
+    from oracle import quant as oq
+    spec, st = inp.spec, inp.structure
+    workers = oa.default_workers()
+    heads = [(0, h) for h in range(8)]
+    t0 = time.perf_counter()
+    kh = np.zeros((1, spec.Hkv, spec.cap, spec.D))
+    vh = np.zeros((1, spec.Hkv, spec.cap, spec.D))
+    for g in range(2):
+        kh[0, g] = oq.dequantize(*oq.quantize(inp.k[0, g], int(st.head_bits[g])))
+        vh[0, g] = oq.dequantize(*oq.quantize(inp.v[0, g], int(st.head_bits[g])))
+    oa.prefill(inp.q, kh, vh, st.seq_lens, heads=heads, workers=workers)
+    dt = time.perf_counter() - t0
+    flops = A.prefill_flops(len(heads), spec.D, st.seq_lens)
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": workers,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "prefill_8k, query heads 0-7 (KV heads 0-1), all 8192 rows; fp64 NumPy, "
+                      f"process pool of {workers} workers, 1 BLAS thread each"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library runs on one GPU; only --gpus 1 is measured "
+              "(sharding is described in the design notes, not run).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_attention_quantized_amd as T
+    import workloads as W
+    from workloads import accounting as A
+
+    torch.cuda.set_device(0)
+    T.device_check(0)
+
+    if args.only == "decode":
+        d = bench_decode(args, torch, T, W, A)
+        print(json.dumps({"decode": d}), flush=True)
+        return
+
+    spec, inp, flops, dt, kern_ms = bench_prefill(args, torch, T, W, A)
+    torch.cuda.empty_cache()
+    dec = None
+    if not args.no_decode and args.only is None:
+        dec = bench_decode(args, torch, T, W, A)
+    cpu = None
+    if not args.no_cpu and args.only is None:
+        log("timing the oracle on a sample")
+        cpu = cpu_baseline(inp, A, W)
+        log(f"oracle: {cpu['seconds']} s, {cpu['value']} TFLOP/s on {cpu['cores']} workers")
+    kern_tf = flops / (kern_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(flops / dt / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "B": spec.B, "Hq": spec.Hq, "Hkv": spec.Hkv,
+                   "head_dim": spec.D, "L": spec.context, "kv_bits": 8, "group": 32,
+                   "mask": "dense causal",
+                   "step": "kv_quantize(K) + kv_quantize(V) + attn_prefill"},
+        "roofline": {"bound": "mfma", "achieved": round(kern_tf, 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kern_tf / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel<4>", "kernel_ms": round(kern_ms, 4),
+                     "flops_per_launch": int(flops)},
+        "cpu_baseline": cpu,
+        "decode": dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
