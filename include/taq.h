@@ -34,12 +34,12 @@
  *   TAQ_LAYOUT_TOKEN (required for K): token t's RB(h) bytes at t * RB(h); in
  *     them channel c's code is byte c (int8) or nibble c % 2 (0 = low) of
  *     byte c / 2 (int4).  scales: fp16 [B][Hkv][C][D/32]; zeros: u8, same shape.
- *   TAQ_LAYOUT_CHANNEL (required for V): tokens in blocks of 128; block j holds
- *     D rows of 128 * bits / 8 bytes; row d holds channel d of the block's 128
- *     tokens: byte t % 128 (int8) or nibble (t % 128) % 2 of byte
- *     (t % 128) / 2 (int4).  scales: fp16 [B][Hkv][D/32][C]; zeros: u8, same.
+ *   TAQ_LAYOUT_CHANNEL (required for V): tokens in blocks of 32; block j holds
+ *     D rows of 32 * bits / 8 bytes; row d holds channel d of the block's 32
+ *     tokens: byte t % 32 (int8) or nibble (t % 32) % 2 of byte (t % 32) / 2
+ *     (int4).  scales: fp16 [B][Hkv][D/32][C]; zeros: u8, same shape.
  *   The channel layout gives the PV matrix product its key-contiguous operand
- *   straight from memory.
+ *   straight from memory, and one 32-token block is one contiguous run.
  * Q, O: fp16 bit patterns, decode [B][Hq][D], prefill [B][Hq][L][D].
  * Skip mask: u8, 1 = compute the 128x128 tile, 0 = skip it; element
  *   data[b*stride_b + g*stride_h + qt*n_k_tiles + kt] for KV head g (strides
@@ -58,7 +58,7 @@
  *   `workspace`, sized by taq_attn_decode_workspace_bytes.
  * - Device pointers must be 16-byte aligned (TAQ_ERR_MISALIGNED otherwise).
  * - Device-resident lengths are clamped to [0, max_seq_len] by the kernels.
- * - softmax_scale = 0 means 1/sqrt(head_dim).
+ * - softmax_scale = 0 means 1/sqrt(head_dim); negative scales are UNSUPPORTED.
  * - Rows with no permitted key (and prefill rows at or beyond the sequence's
  *   length) are written as zeros.
  */

@@ -26,10 +26,11 @@ per-head bit widths bits[h] and RB(h) = D * bits[h] / 8 code bytes per token:
 * "token" layout (used for K): token t's RB(h) bytes sit at t * RB(h); within
   them channel c's code is byte c (int8) or nibble c % 2 of byte c // 2 (int4).
   scales fp16 [B][Hkv][cap][G], zeros u8 [B][Hkv][cap][G], G = D / 32.
-* "channel" layout (used for V): tokens come in blocks of 128; block j of a
-  head holds D rows of 128 * bits / 8 bytes; row d has token t's code for
-  channel d at byte t % 128 (int8) or nibble (t % 128) % 2 of byte
-  (t % 128) // 2 (int4).  scales fp16 [B][Hkv][G][cap], zeros u8 [B][Hkv][G][cap].
+* "channel" layout (used for V): tokens come in blocks of 32; block j of a
+  head holds D rows of 32 * bits / 8 bytes; row d has token t's code for
+  channel d at byte t % 32 (int8) or nibble (t % 32) % 2 of byte
+  (t % 32) // 2 (int4).  scales fp16 [B][Hkv][G][cap], zeros u8 [B][Hkv][G][cap].
+  The capacity is a multiple of 128 (the KV-tile size) in both layouts.
 
 Pins (tests/test_oracle_quant.py): exact-rational re-derivation of s, z and c
 per group (``oracle.exact``), a division-free brute-force nearest-code search,
@@ -42,7 +43,8 @@ from __future__ import annotations
 import numpy as np
 
 GROUP = 32
-BLOCK = 128
+BLOCK = 32      # tokens per block of the channel layout
+CAP_MULTIPLE = 128
 
 
 def _fp16_ceil_div(span: np.ndarray, qmax: int) -> np.ndarray:
@@ -155,7 +157,7 @@ class Cache:
                  layout: str):
         if layout not in ("token", "channel"):
             raise ValueError(layout)
-        if cap % BLOCK:
+        if cap % CAP_MULTIPLE:
             raise ValueError("capacity must be a multiple of 128")
         self.B, self.Hkv, self.D, self.cap = B, Hkv, D, cap
         self.bits = [int(b) for b in head_bits]

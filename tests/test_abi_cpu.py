@@ -111,6 +111,7 @@ def test_attention_rejects(call):
     assert call(q=0)[0] == INVALID
     assert call(o=FAKE + 2)[0] == MISALIGNED
     assert call(scale=float("nan"))[0] == INVALID
+    assert call(scale=-0.5)[0] == UNSUPPORTED
     kd = cache(B=1, H=2, cap=256, bits=(8, 8), layout=1)
     assert call(k=kd)[0] == UNSUPPORTED                  # K must be token layout
     vd = cache(B=1, H=2, cap=256, bits=(8, 8), layout=0)

@@ -217,24 +217,26 @@ def test_token_layout_mixed_heads():
 
 def test_channel_layout_int8_and_int4():
     cache = quant.Cache(1, 2, 32, 256, [8, 4], "channel")
-    # head 0 int8: token t, channel d at block t//128, byte d*128 + t%128
+    # head 0 int8: token t, channel d at block t//32 (32*32 bytes each),
+    # byte d*32 + t%32
     codes = np.zeros((256, 32), np.uint8)
-    codes[130, 7] = 201
-    codes[3, 31] = 17
+    codes[130, 7] = 201      # block 4, row 7, byte 2
+    codes[3, 31] = 17        # block 0, row 31, byte 3
     cache.write(0, 0, 0, codes, np.ones((256, 1), np.float16), np.zeros((256, 1), np.uint8))
     slab0 = cache.codes[:256 * 32]
-    assert slab0[1 * 128 * 32 + 7 * 128 + 2] == 201
-    assert slab0[0 * 128 * 32 + 31 * 128 + 3] == 17
+    assert slab0[4 * 1024 + 7 * 32 + 2] == 201
+    assert slab0[0 * 1024 + 31 * 32 + 3] == 17
     assert int(np.count_nonzero(slab0)) == 2
-    # head 1 int4: byte d*64 + (t%128)//2, low nibble for even t
+    # head 1 int4: block t//32 of 32*16 bytes, byte d*16 + (t%32)//2,
+    # low nibble for even t
     codes = np.zeros((256, 32), np.uint8)
     codes[4, 2] = 9
     codes[5, 2] = 6
-    codes[129, 0] = 15
+    codes[129, 0] = 15       # block 4, row 0, byte 0, high nibble
     cache.write(0, 1, 0, codes, np.ones((256, 1), np.float16), np.zeros((256, 1), np.uint8))
     slab1 = cache.codes[256 * 32:]
-    assert slab1[2 * 64 + 2] == (9 | (6 << 4))
-    assert slab1[1 * 32 * 64 + 0 * 64 + 0] == (15 << 4)
+    assert slab1[0 * 512 + 2 * 16 + 2] == (9 | (6 << 4))
+    assert slab1[4 * 512 + 0 * 16 + 0] == (15 << 4)
     assert cache.scales.shape == (1, 2, 1, 256)
     assert np.array_equal(cache.read_codes(0, 1), codes)
 

@@ -241,6 +241,8 @@ taq_status taq_attn_decode(const taq_kv_cache* k, const taq_kv_cache* v, const v
     return fail(TAQ_ERR_MISALIGNED, "q, o and seq_lens must be 16-byte aligned");
   if (!std::isfinite(softmax_scale))
     return fail(TAQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (softmax_scale < 0.f)
+    return fail(TAQ_ERR_UNSUPPORTED, "softmax_scale must be >= 0 (0 selects 1/sqrt(head_dim))");
   st = check_mask(mask, 1, (max_len + TAQ_TILE - 1) / TAQ_TILE);
   if (st) return st;
   const size_t need = taq_attn_decode_workspace_bytes(k, hq, max_len);
@@ -285,6 +287,8 @@ taq_status taq_attn_prefill(const taq_kv_cache* k, const taq_kv_cache* v, const 
     return fail(TAQ_ERR_MISALIGNED, "q, o and seq_lens must be 16-byte aligned");
   if (!std::isfinite(softmax_scale))
     return fail(TAQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (softmax_scale < 0.f)
+    return fail(TAQ_ERR_UNSUPPORTED, "softmax_scale must be >= 0 (0 selects 1/sqrt(head_dim))");
   const int nt = (max_len + TAQ_TILE - 1) / TAQ_TILE;
   st = check_mask(mask, nt, nt);
   if (st) return st;

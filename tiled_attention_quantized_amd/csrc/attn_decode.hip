@@ -8,12 +8,14 @@
 // section 5.3), skipping KV tiles the block mask drops (section 2.3).
 //
 // Work decomposition (gfx950, wave64):
-//  * grid = (KV chunk, KV head, batch); a 256-thread workgroup owns one chunk
+//  * one workgroup per (KV chunk, KV head, batch); a 256-thread workgroup owns one chunk
 //    of `chunk` tokens of one (batch, KV head) and serves all r = Hq/Hkv query
 //    heads of that KV head, so each K/V byte is read once.
 //  * each of the 4 waves streams chunk/4 tokens in steps of 32 tokens and keeps
-//    its own (max, normaliser, accumulator); the waves merge through LDS and the
-//    workgroup writes one partial triple per query head to the workspace;
+//    its own (max, normaliser, accumulator).  The loads of the next step are
+//    issued before the current step is computed (register double buffering).
+//    The waves merge through LDS and the workgroup writes one partial triple
+//    per query head.
 //  * a second kernel merges the chunk partials of each (batch, query head) in
 //    chunk order and writes fp16 O.
 //
@@ -23,8 +25,10 @@
 //    ends up with the 4 per-group partial dot products of one (head, token) and
 //    applies the 4 group scales itself: score = sum_g s_g * dot_g.
 //  * PV: A = V-hat^T (rows = channels) dequantised to fp16 in registers from
-//    the channel-major V layout (8 consecutive tokens of one channel per lane),
-//    B = P^T gathered across lanes with ds_bpermute; O^T accumulates in fp32.
+//    the channel-major V layout (8 consecutive tokens of one channel per lane;
+//    a lane's 8 channels 8*i16 .. +7 share one quantisation group, so it needs
+//    one group's scales and zeros), B = P^T gathered across lanes with
+//    ds_bpermute; O^T accumulates in fp32.
 #include "taq_internal.h"
 #include "device_common.h"
 
@@ -49,7 +53,7 @@ template <bool V8>
 __device__ __forceinline__ uint32_t v_negz_pair(u32x2 z8, int m) {
   if (V8) {
     const uint32_t w = m < 2 ? z8[0] : z8[1];
-    return perm_b32(0xE4E4E4E4u, w, (m & 1) ? 0x04030402u : 0x04010400u);
+    return perm_b32(vconst(0xE4E4E4E4u), w, (m & 1) ? 0x04030402u : 0x04010400u);
   }
   const uint32_t sel = (uint32_t)m | (0x0Cu << 8) | ((uint32_t)(4 + m) << 16) | (0x0Cu << 24);
   return perm_b32(z8[1], z8[0], sel) | 0xE400E400u;
@@ -68,34 +72,227 @@ __device__ __forceinline__ uint32_t v_code_pair(u32x2 c8, int m) {
   return nibbles_to_biased_h2(c8[0], m);
 }
 
-// Token index (0..7 within a lane's 8) of half `hh` of pair m.
-template <bool V8>
-__device__ __forceinline__ int v_pair_token(int m, int hh) {
-  return V8 ? 2 * m + hh : m + 4 * hh;
+// Raw bytes of one 32-token step held by one lane.
+struct StepData {
+  u32x4 kc[2][2];   // K codes of the lane's two tokens (group lg); int4 uses [bk][0]
+  uint32_t kz[2];   // K zero bytes of those tokens (group lg)
+  u32x2 ks[2];      // K scales of those tokens (all 4 groups)
+  u32x2 vc[8];      // V codes: channel 8*i16 + db, tokens 8*lg .. +7 (int4: vc[db][0])
+  u32x2 vz;         // V zeros of the lane's 8 tokens (group i16 / 4)
+  u32x4 vs;         // V scales of the lane's 8 tokens (group i16 / 4)
+};
+
+struct Ptrs {
+  const uint8_t* kbase;
+  const uint8_t* vbase;
+  const uint16_t* kscale;
+  const uint8_t* kzero;
+  const uint16_t* vscale;
+  const uint8_t* vzero;
+  int cap;
+};
+
+// Loads of one 32-token step starting at t0 (a multiple of 32).  Offsets
+// inside one (batch, KV head) slab fit in 32 bits (at most capacity * 128
+// bytes), so every address is a uniform base plus a 32-bit lane offset.
+template <bool K8, bool V8>
+__device__ __forceinline__ void load_step(const Ptrs& p, int t0, int i16, int lg, StepData& s) {
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk) {
+    const uint32_t T = (uint32_t)(t0 + qk_token<V8>(bk, i16));
+    if (K8) {
+      const u32x4* kp = reinterpret_cast<const u32x4*>(p.kbase + (T * D + 32 * lg));
+      s.kc[bk][0] = kp[0];
+      s.kc[bk][1] = kp[1];
+    } else {
+      s.kc[bk][0] = *reinterpret_cast<const u32x4*>(p.kbase + (T * (D / 2) + 16 * lg));
+    }
+    s.kz[bk] = p.kzero[T * 4 + lg];
+    s.ks[bk] = *reinterpret_cast<const u32x2*>(p.kscale + T * 4);
+  }
+  // one V block of D channel rows per step
+  const uint8_t* vblk = p.vbase + (uint32_t)(t0 >> 5) * (uint32_t)(D * (V8 ? 32 : 16));
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    const uint32_t d = 8 * i16 + db;
+    if (V8) {
+      s.vc[db] = *reinterpret_cast<const u32x2*>(vblk + (d * 32 + 8 * lg));
+    } else {
+      s.vc[db][0] = *reinterpret_cast<const uint32_t*>(vblk + (d * 16 + 4 * lg));
+      s.vc[db][1] = 0u;
+    }
+  }
+  const uint32_t mo = (uint32_t)(i16 >> 2) * (uint32_t)p.cap + (uint32_t)(t0 + 8 * lg);
+  s.vz = *reinterpret_cast<const u32x2*>(p.vzero + mo);
+  s.vs = *reinterpret_cast<const u32x4*>(p.vscale + mo);
 }
 
 template <int R, bool K8, bool V8>
-__device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n,
-                            float* lds) {
+struct WaveState {
+  static constexpr int NRB = (R + 3) / 4;
+  half8 aq[NRB][4];
+  float m_run[NRB], l_run[NRB];
+  f32x4 acc[8];
+};
+
+template <int R, bool K8, bool V8>
+__device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K8, V8>& ws,
+                                             StepData& s, int nvalid, int i16, int lg) {
+  constexpr int NRB = WaveState<R, K8, V8>::NRB;
+  // ---------------- scores ----------------
+  float sc[NRB][2];
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk) {
+    const int tl = qk_token<V8>(bk, i16);
+    const uint32_t nz = neg_biased_zero_h2(s.kz[bk]);
+    half8 bk8[4];
+    if (K8) {
+      const uint32_t wv[8] = {s.kc[bk][0][0], s.kc[bk][0][1], s.kc[bk][0][2], s.kc[bk][0][3],
+                              s.kc[bk][1][0], s.kc[bk][1][1], s.kc[bk][1][2], s.kc[bk][1][3]};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t h2 = bytes_to_biased_h2(wv[2 * kk + (k >> 1)], k & 1);
+          o[k] = h2_to_u32(u32_to_h2(h2) + u32_to_h2(nz));
+        }
+        bk8[kk] = u4_to_h8(o);
+      }
+    } else {
+      const u32x4 cw = s.kc[bk][0];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t h2 = nibbles_to_biased_h2(cw[kk], k);
+          o[k] = h2_to_u32(u32_to_h2(h2) + u32_to_h2(nz));
+        }
+        bk8[kk] = u4_to_h8(o);
+      }
+    }
+    const u32x2 sraw = s.ks[bk];
+    const float s0 = (float)u32_to_h2(sraw[0])[0], s1 = (float)u32_to_h2(sraw[0])[1];
+    const float s2 = (float)u32_to_h2(sraw[1])[0], s3 = (float)u32_to_h2(sraw[1])[1];
+    const bool valid = tl < nvalid;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) d4 = mfma16x16x32(ws.aq[rb][kk], bk8[kk], d4);
+      float x = s0 * d4[0];
+      x = fmaf(s1, d4[1], x);
+      x = fmaf(s2, d4[2], x);
+      x = fmaf(s3, d4[3], x);
+      x *= a.scale_log2;
+      const bool live = 4 * rb + lg < R;
+      sc[rb][bk] = valid ? (live ? x : 0.f) : -INFINITY;
+    }
+  }
+
+  // ---------------- online softmax ----------------
+  // The running maximum m is only moved when the tile maximum exceeds it by
+  // more than 2^8 (log2 units): weights exp2(s - m) then stay below 256, exact
+  // enough in fp16, and the accumulator is rescaled only on those steps.  The
+  // final O = acc / l is unchanged by the choice of m.
+  uint32_t p2[NRB];
+  float alpha[NRB];
+  bool any_move = false;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const float mx = row16_max(fmaxf(sc[rb][0], sc[rb][1]));
+    const bool move = mx > ws.m_run[rb] + 8.f;
+    const float mn = move ? mx : ws.m_run[rb];
+    alpha[rb] = move ? fast_exp2(ws.m_run[rb] - mn) : 1.f;
+    any_move |= move;
+    ws.m_run[rb] = mn;
+    const _Float16 p0 = (_Float16)fast_exp2(sc[rb][0] - mn);
+    const _Float16 p1 = (_Float16)fast_exp2(sc[rb][1] - mn);
+    ws.l_run[rb] = fmaf(ws.l_run[rb], alpha[rb], (float)p0 + (float)p1);
+    p2[rb] = h2_to_u32(half2v{p0, p1});
+  }
+  const bool rescale = __any(any_move);
+
+  // ---------------- gather P^T and alpha into the PV layout ----------------
+  const int hcol = i16;
+  const int hsrc = (hcol & 3) * 16;
+  u32x4 pb;
+#pragma unroll
+  for (int mm = 0; mm < 4; ++mm) {
+    const int src = hsrc + 4 * lg + mm;
+    uint32_t v = lane_read(p2[0], src);
+    if (NRB > 1) {
+      const uint32_t v1 = lane_read(p2[NRB - 1], src);
+      v = (hcol >> 2) ? v1 : v;
+    }
+    pb[mm] = hcol < R ? v : 0u;
+  }
+  if (rescale) {
+    // rare: keep it a real branch (an empty volatile asm stops the compiler
+    // from turning it into an unconditional multiply by a selected factor)
+    asm volatile("" ::: "memory");
+    float al = lane_read_f(alpha[0], hsrc);
+    if (NRB > 1) {
+      const float a1 = lane_read_f(alpha[NRB - 1], hsrc);
+      al = (hcol >> 2) ? a1 : al;
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) ws.acc[db] = ws.acc[db] * al;
+  }
+  const half8 bp = u4_to_h8(pb);
+
+  // ---------------- V-hat^T operand and PV ----------------
+  // zero the scales of tokens past the end so their V-hat is exactly 0
+  // (branch-free selects: no divergent control flow inside the step)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ta = 8 * lg + 2 * j;
+    const uint32_t keep = (ta < nvalid ? 0x0000FFFFu : 0u) | (ta + 1 < nvalid ? 0xFFFF0000u : 0u);
+    s.vs[j] &= keep;
+  }
+  uint32_t nzp[4], scp[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    nzp[m] = v_negz_pair<V8>(s.vz, m);
+    scp[m] = v_scale_pair<V8>(s.vs, m);
+  }
+#pragma unroll
+  for (int db = 0; db < 8; ++db) {
+    u32x4 o;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const half2v cz = u32_to_h2(v_code_pair<V8>(s.vc[db], m)) + u32_to_h2(nzp[m]);
+      o[m] = h2_to_u32(cz * u32_to_h2(scp[m]));
+    }
+    ws.acc[db] = mfma16x16x32(u4_to_h8(o), bp, ws.acc[db]);
+  }
+}
+
+template <int R, bool K8, bool V8>
+__device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, float* lds) {
   constexpr int NRB = (R + 3) / 4;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  // wave index as a scalar: all token-range and loop control below is
+  // wave-uniform, so it runs on the scalar unit with real branches
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15;
   const int lg = lane >> 4;
 
   const CacheGeom& K = a.k;
   const CacheGeom& V = a.v;
   const int G = D / 32;
-  const uint8_t* kbase = K.codes + (int64_t)b * K.bstride + K.hoff[g];
-  const uint8_t* vbase = V.codes + (int64_t)b * V.bstride + V.hoff[g];
-  const uint16_t* kscale = K.scales + ((int64_t)b * K.H + g) * K.cap * G;
-  const uint8_t* kzero = K.zeros + ((int64_t)b * K.H + g) * K.cap * G;
-  const uint16_t* vscale = V.scales + ((int64_t)b * V.H + g) * G * (int64_t)V.cap;
-  const uint8_t* vzero = V.zeros + ((int64_t)b * V.H + g) * G * (int64_t)V.cap;
-  const int cap = K.cap;
+  Ptrs p;
+  p.kbase = K.codes + (int64_t)b * K.bstride + K.hoff[g];
+  p.vbase = V.codes + (int64_t)b * V.bstride + V.hoff[g];
+  p.kscale = K.scales + ((int64_t)b * K.H + g) * K.cap * G;
+  p.kzero = K.zeros + ((int64_t)b * K.H + g) * K.cap * G;
+  p.vscale = V.scales + ((int64_t)b * V.H + g) * G * (int64_t)V.cap;
+  p.vzero = V.zeros + ((int64_t)b * V.H + g) * G * (int64_t)V.cap;
+  p.cap = K.cap;
 
+  WaveState<R, K8, V8> ws;
   // ---- Q as the block-diagonal A operand ------------------------------------
-  half8 aq[NRB][4];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const int hl = 4 * rb + (i16 >> 2);
@@ -120,163 +317,56 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n,
           o[k] = perm_b32(hi, lo, (k & 1) ? 0x07060302u : 0x05040100u);
         }
       }
-      aq[rb][kk] = u4_to_h8(o);
+      ws.aq[rb][kk] = u4_to_h8(o);
     }
   }
-
-  // ---- wave state ------------------------------------------------------------
-  float m_run[NRB], l_run[NRB];
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) { m_run[rb] = NEG_BIG; l_run[rb] = 0.f; }
-  f32x4 acc[8];
+  for (int rb = 0; rb < NRB; ++rb) { ws.m_run[rb] = NEG_BIG; ws.l_run[rb] = 0.f; }
 #pragma unroll
-  for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < 8; ++db) ws.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int per_wave = a.chunk / WAVES;
   const int t_begin = c * a.chunk + w * per_wave;
   const int t_end = min(t_begin + per_wave, n);
-  const uint8_t* mrow = a.mask ? a.mask + (int64_t)b * a.mask_sb + (int64_t)g * a.mask_sh
-                               : nullptr;
+  const int t_safe = c * a.chunk;   // a valid step address (c * chunk < n)
 
-  for (int t0 = t_begin; t0 < t_end; t0 += STEP) {
-    if (mrow && !mrow[t0 >> 7]) continue;
-    const int nvalid = t_end - t0;  // tokens t0 .. t0+nvalid-1 are valid (if < 32)
+  // KV-tile keep bits of the tiles this wave touches (at most 9 tiles of 128
+  // tokens), read once so that the step loop does no mask loads.
+  const int tile0 = t_begin >> 7;
+  uint32_t tbits = 0xFFFFFFFFu;
+  if (a.mask && t_begin < t_end) {
+    const uint8_t* mrow = a.mask + (int64_t)b * a.mask_sb + (int64_t)g * a.mask_sh;
+    const int tile1 = (t_end - 1) >> 7;
+    tbits = 0;
+    for (int k = 0; k <= tile1 - tile0; ++k) tbits |= (mrow[tile0 + k] ? 1u : 0u) << k;
+  }
+  auto next_step = [&](int t) -> int {
+    while (t < t_end && !((tbits >> ((t >> 7) - tile0)) & 1u)) t += STEP;
+    return t;
+  };
 
-    // ---------------- scores ----------------
-    float sc[NRB][2];
-#pragma unroll
-    for (int bk = 0; bk < 2; ++bk) {
-      const int tl = qk_token<V8>(bk, i16);
-      const int T = t0 + tl;
-      // B operand: (c - z) for token T, channels of group lg
-      const uint32_t nz = neg_biased_zero_h2(kzero[(int64_t)T * G + lg]);
-      half8 bk8[4];
-      if (K8) {
-        const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + (int64_t)T * D + 32 * lg);
-        const u32x4 c0 = kp[0], c1 = kp[1];
-        const uint32_t wv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          u32x4 o;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t h2 = bytes_to_biased_h2(wv[2 * kk + (k >> 1)], k & 1);
-            o[k] = h2_to_u32(u32_to_h2(h2) + u32_to_h2(nz));
-          }
-          bk8[kk] = u4_to_h8(o);
-        }
-      } else {
-        const u32x4 cw = *reinterpret_cast<const u32x4*>(kbase + (int64_t)T * (D / 2) + 16 * lg);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          u32x4 o;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t h2 = nibbles_to_biased_h2(cw[kk], k);
-            o[k] = h2_to_u32(u32_to_h2(h2) + u32_to_h2(nz));
-          }
-          bk8[kk] = u4_to_h8(o);
-        }
-      }
-      // scales of token T for the epilogue (all 4 groups)
-      const u32x2 sraw = *reinterpret_cast<const u32x2*>(kscale + (int64_t)T * G);
-      const float s0 = (float)u32_to_h2(sraw[0])[0], s1 = (float)u32_to_h2(sraw[0])[1];
-      const float s2 = (float)u32_to_h2(sraw[1])[0], s3 = (float)u32_to_h2(sraw[1])[1];
-      const bool valid = tl < nvalid;
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) d4 = mfma16x16x32(aq[rb][kk], bk8[kk], d4);
-        float s = s0 * d4[0];
-        s = fmaf(s1, d4[1], s);
-        s = fmaf(s2, d4[2], s);
-        s = fmaf(s3, d4[3], s);
-        s *= a.scale_log2;
-        const bool live = 4 * rb + lg < R;
-        sc[rb][bk] = valid ? (live ? s : 0.f) : -INFINITY;
-      }
-    }
-
-    // ---------------- online softmax ----------------
-    uint32_t p2[NRB];
-    float alpha[NRB];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const float mx = row16_max(fmaxf(sc[rb][0], sc[rb][1]));
-      const float mn = fmaxf(m_run[rb], mx);
-      alpha[rb] = fast_exp2(m_run[rb] - mn);
-      m_run[rb] = mn;
-      const _Float16 p0 = (_Float16)fast_exp2(sc[rb][0] - mn);
-      const _Float16 p1 = (_Float16)fast_exp2(sc[rb][1] - mn);
-      l_run[rb] = fmaf(l_run[rb], alpha[rb], (float)p0 + (float)p1);
-      p2[rb] = h2_to_u32(half2v{p0, p1});
-    }
-
-    // ---------------- gather P^T and alpha into the PV layout ----------------
-    const int hcol = i16;                 // PV column = query head
-    const int hsrc = (hcol & 3) * 16;     // QK row of that head
-    u32x4 pb;
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-      const int src = hsrc + 4 * lg + mm;
-      uint32_t v = lane_read(p2[0], src);
-      if (NRB > 1) {
-        const uint32_t v1 = lane_read(p2[NRB - 1], src);
-        v = (hcol >> 2) ? v1 : v;
-      }
-      pb[mm] = hcol < R ? v : 0u;
-    }
-    float al = lane_read_f(alpha[0], hsrc);
-    if (NRB > 1) {
-      const float a1 = lane_read_f(alpha[NRB - 1], hsrc);
-      al = (hcol >> 2) ? a1 : al;
-    }
-    const half8 bp = u4_to_h8(pb);
-
-    // ---------------- V-hat^T operand and PV ----------------
-    const int blk = t0 >> 7;
-    const int tt = (t0 & 127) + 8 * lg;    // first of this lane's 8 tokens in the block
-    u32x2 vz[4];
-    u32x4 vs[4];
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      vz[gq] = *reinterpret_cast<const u32x2*>(vzero + (int64_t)gq * cap + t0 + 8 * lg);
-      vs[gq] = *reinterpret_cast<const u32x4*>(vscale + (int64_t)gq * cap + t0 + 8 * lg);
-    }
-    if (nvalid < STEP) {
-      // zero the scales of tokens past the end so their V-hat is exactly 0
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t wv = vs[gq][j];
-          const int ta = 8 * lg + 2 * j, tb = ta + 1;
-          if (ta >= nvalid) wv &= 0xFFFF0000u;
-          if (tb >= nvalid) wv &= 0x0000FFFFu;
-          vs[gq][j] = wv;
-        }
-    }
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const int d = 16 * db + i16;
-      const int gq = db >> 1;
-      const uint8_t* row = vbase + ((int64_t)blk * D + d) * (V8 ? 128 : 64);
-      u32x2 cw;
-      if (V8) {
-        cw = *reinterpret_cast<const u32x2*>(row + tt);
-      } else {
-        cw[0] = *reinterpret_cast<const uint32_t*>(row + tt / 2);
-        cw[1] = 0;
-      }
-      u32x4 o;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const half2v cz = u32_to_h2(v_code_pair<V8>(cw, m)) + u32_to_h2(v_negz_pair<V8>(vz[gq], m));
-        o[m] = h2_to_u32(cz * u32_to_h2(v_scale_pair<V8>(vs[gq], m)));
-      }
-      acc[db] = acc[db] * al;
-      acc[db] = mfma16x16x32(u4_to_h8(o), bp, acc[db]);
+  // ---- two-buffer pipeline over the wave's steps -----------------------------
+  // The loads of the next step are issued before the current step is
+  // computed.  Every iteration issues exactly one step of loads (past the end:
+  // a repeat of a valid step that is never used), so the number of loads in
+  // flight is the same on every path and each wait before a use is partial.
+  StepData A, Bf;
+  int t_cur = next_step(t_begin);
+  if (t_cur < t_end) {
+    load_step<K8, V8>(p, t_cur, i16, lg, A);
+    int t_nxt = next_step(t_cur + STEP);
+    load_step<K8, V8>(p, t_nxt < t_end ? t_nxt : t_safe, i16, lg, Bf);
+    while (true) {
+      compute_step<R, K8, V8>(a, ws, A, t_end - t_cur, i16, lg);
+      t_cur = t_nxt;
+      if (t_cur >= t_end) break;
+      t_nxt = next_step(t_cur + STEP);
+      load_step<K8, V8>(p, t_nxt < t_end ? t_nxt : t_safe, i16, lg, A);
+      compute_step<R, K8, V8>(a, ws, Bf, t_end - t_cur, i16, lg);
+      t_cur = t_nxt;
+      if (t_cur >= t_end) break;
+      t_nxt = next_step(t_cur + STEP);
+      load_step<K8, V8>(p, t_nxt < t_end ? t_nxt : t_safe, i16, lg, Bf);
     }
   }
 
@@ -287,10 +377,10 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n,
   float* so = lds + 2 * WAVES * R;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const float lt = row16_sum(l_run[rb]);
+    const float lt = row16_sum(ws.l_run[rb]);
     const int h = 4 * rb + lg;
     if (i16 == 0 && h < R) {
-      sm[w * R + h] = m_run[rb];
+      sm[w * R + h] = ws.m_run[rb];
       sl[w * R + h] = lt;
     }
   }
@@ -299,7 +389,7 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n,
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        so[(w * R + i16) * D + 16 * db + 4 * lg + v] = acc[db][v];
+        so[(w * R + i16) * D + 32 * lg + 8 * v + db] = ws.acc[db][v];
   }
   __syncthreads();
   const int nchunk = a.nchunk;
@@ -324,68 +414,116 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n,
   }
 }
 
-template <int R>
+#ifndef TAQ_DECODE_WAVES_INT4
+#define TAQ_DECODE_WAVES_INT4 3
+#endif
+template <int R, bool K8, bool V8>
 __global__ void __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu((K8 || V8) ? 2 : TAQ_DECODE_WAVES_INT4, (K8 || V8) ? 2 : TAQ_DECODE_WAVES_INT4)))
 decode_split_kernel(DecodeArgs a) {
   __shared__ float lds[2 * WAVES * R + WAVES * R * D];
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int units = a.k.B * a.nheads;
+#ifdef TAQ_DECODE_CHUNK_FASTEST
+  const int u = blockIdx.x / a.nchunk;
+  const int c = blockIdx.x - u * a.nchunk;
+#else
+  const int c = blockIdx.x / units;
+  const int u = blockIdx.x - c * units;
+#endif
+  const int b = u / a.nheads;
+  const int g = a.heads[u - b * a.nheads];
   int n = a.lens[b];
   n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
   if (c * a.chunk >= n) return;
-  const bool k8 = (a.k.is8 >> g) & 1ull, v8 = (a.v.is8 >> g) & 1ull;
-  if (k8) {
-    if (v8) decode_body<R, true, true>(a, b, g, c, n, lds);
-    else decode_body<R, true, false>(a, b, g, c, n, lds);
-  } else {
-    if (v8) decode_body<R, false, true>(a, b, g, c, n, lds);
-    else decode_body<R, false, false>(a, b, g, c, n, lds);
-  }
+  decode_body<R, K8, V8>(a, b, g, c, n, lds);
 }
 
-// One workgroup of D threads per (batch, query head).
-__global__ void __launch_bounds__(128)
+// One wave per (batch, query head): lanes own chunks for the max / normaliser
+// and channel pairs (2 * lane, 2 * lane + 1) for the accumulator.
+__global__ void __launch_bounds__(256)
 decode_merge_kernel(DecodeArgs a) {
-  const int bh = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= a.k.B * a.Hq) return;
   const int b = bh / a.Hq;
-  const int d = threadIdx.x;
   int n = a.lens[b];
   n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
   const int nc = (n + a.chunk - 1) / a.chunk;
   const float* src = a.ws + (int64_t)bh * a.nchunk * (D + 2);
   float M = NEG_BIG;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, src[c * (D + 2)]);
-  float o = 0.f, l = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float* p = src + c * (D + 2);
-    const float f = fast_exp2(p[0] - M);
-    l = fmaf(p[1], f, l);
-    o = fmaf(p[2 + d], f, o);
+  for (int c = lane; c < nc; c += 64) M = fmaxf(M, src[(int64_t)c * (D + 2)]);
+  M = fmaxf(M, __shfl_xor(M, 32));
+  M = row16_max(fmaxf(M, __shfl_xor(M, 16)));
+  float l = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int c0 = 0; c0 < nc; c0 += 64) {
+    const int c = c0 + lane;
+    float f = 0.f;
+    if (c < nc) {
+      f = fast_exp2(src[(int64_t)c * (D + 2)] - M);
+      l = fmaf(src[(int64_t)c * (D + 2) + 1], f, l);
+    }
+    const int cn = min(64, nc - c0);
+#pragma unroll 8
+    for (int j = 0; j < cn; ++j) {
+      const float fj = __shfl(f, j);
+      const float2 v = *reinterpret_cast<const float2*>(src + (int64_t)(c0 + j) * (D + 2) + 2 + 2 * lane);
+      o0 = fmaf(v.x, fj, o0);
+      o1 = fmaf(v.y, fj, o1);
+    }
   }
-  const float r = l > 0.f ? o / l : 0.f;
-  a.o[(int64_t)bh * D + d] = half_to_bits((_Float16)r);
+  l += __shfl_xor(l, 32);
+  l = row16_sum(l + __shfl_xor(l, 16));
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  half2v h = {(_Float16)(o0 * inv), (_Float16)(o1 * inv)};
+  *reinterpret_cast<half2v*>(a.o + (int64_t)bh * D + 2 * lane) = h;
 }
 
 }  // namespace
 
 int decode_chunk_tokens(int B, int Hkv, int max_len) {
-  int chunk = 128;
+  // Largest chunk (<= 4096 tokens) that still gives >= 2048 workgroups, so
+  // every CU gets several; at least 128 (32 tokens per wave).
+  int chunk = 4096;
   const int64_t units = (int64_t)B * Hkv;
-  while (chunk < 2048 && units * ((max_len + 2 * chunk - 1) / (2 * chunk)) >= 1024) chunk *= 2;
+  while (chunk > 128 && units * ((max_len + chunk - 1) / chunk) < 2048) chunk /= 2;
   return chunk;
 }
 
+template <int R>
+hipError_t launch_variants(DecodeArgs a, hipStream_t s) {
+  // group the KV heads by their (K bits, V bits) variant
+  for (int var = 0; var < 4; ++var) {
+    const bool k8 = var & 2, v8 = var & 1;
+    a.nheads = 0;
+    for (int h = 0; h < a.k.H; ++h)
+      if ((((a.k.is8 >> h) & 1ull) != 0) == k8 && (((a.v.is8 >> h) & 1ull) != 0) == v8)
+        a.heads[a.nheads++] = (uint8_t)h;
+    if (a.nheads == 0) continue;
+    const dim3 grid(a.nchunk * a.nheads * a.k.B);
+    switch (var) {
+      case 0: hipLaunchKernelGGL((decode_split_kernel<R, false, false>), grid, dim3(256), 0, s, a); break;
+      case 1: hipLaunchKernelGGL((decode_split_kernel<R, false, true>), grid, dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((decode_split_kernel<R, true, false>), grid, dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL((decode_split_kernel<R, true, true>), grid, dim3(256), 0, s, a); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.nchunk, a.k.H, a.k.B);
+  hipError_t e;
   switch (a.r) {
-    case 1: hipLaunchKernelGGL(decode_split_kernel<1>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(decode_split_kernel<2>, grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(decode_split_kernel<4>, grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(decode_split_kernel<8>, grid, dim3(256), 0, s, a); break;
+    case 1: e = launch_variants<1>(a, s); break;
+    case 2: e = launch_variants<2>(a, s); break;
+    case 4: e = launch_variants<4>(a, s); break;
+    case 8: e = launch_variants<8>(a, s); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.k.B * a.Hq), dim3(128), 0, s, a);
+  const int nbh = a.k.B * a.Hq;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((nbh + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

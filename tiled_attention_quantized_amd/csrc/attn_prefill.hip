@@ -13,8 +13,9 @@
 //    r = Hq/Hkv query heads that share one KV head, so every K/V tile is
 //    fetched and dequantised once for r * BQ = 256 (head, row) pairs; wave w
 //    takes head w % r and the 32 rows (w / r) * 32 .. +31;
-//  * the key loop runs in tiles of 64 keys; the next needed tile is fetched
-//    from HBM into registers while the current one is consumed from LDS;
+//  * the key loop runs in tiles of 64 keys through two LDS stages: while
+//    tile i is consumed, tile i+1 is dequantised into the other stage and
+//    tile i+2 is fetched from HBM into registers (one barrier per tile);
 //  * both contractions use v_mfma_f32_32x32x16_f16 in transposed form:
 //    S^T = K-hat Q^T (A = K-hat tile from LDS, B = Q held in registers) and
 //    O^T += V-hat^T P^T (A = V-hat^T tile from LDS, B = P straight from the
@@ -35,6 +36,7 @@ constexpr int KS_STRIDE = D * 2 + 16;  // bytes per K-hat row in LDS (padded)
 constexpr int VS_STRIDE = KT * 2 + 16; // bytes per V-hat^T row in LDS (padded)
 constexpr int LDS_K = KT * KS_STRIDE;
 constexpr int LDS_V = D * VS_STRIDE;
+constexpr int LDS_STAGE = LDS_K + LDS_V;   // one tile (K-hat and V-hat^T)
 constexpr float NEG_BIG = -1.0e30f;
 
 // Natural-order nibble pair: channels / keys 2j and 2j+1 of the 8 nibbles in w.
@@ -83,8 +85,9 @@ __device__ __forceinline__ void stage_load(const TileCtx& c, int kt0, int tid, S
   {
     const int d = tid >> 2, q = tid & 3;
     const int grp = d >> 5;
-    const int blk = kt0 >> 7, kin = (kt0 & 127) + 16 * q;
-    const uint8_t* row = c.vbase + ((int64_t)blk * D + d) * (V8 ? 128 : 64);
+    const int key = kt0 + 16 * q;
+    const int blk = key >> 5, kin = key & 31;
+    const uint8_t* row = c.vbase + ((int64_t)blk * D + d) * (V8 ? 32 : 16);
     if (V8) {
       s.vc = *reinterpret_cast<const u32x4*>(row + kin);
     } else {
@@ -152,7 +155,8 @@ template <int R, bool K8, bool V8>
 __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n, char* lds) {
   constexpr int BQ = 32 * (NWAVE / R);
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int i32 = lane & 31, hb = lane >> 5;
   const int hl = w % R, rblk = w / R;
   const int hq = g * R + hl;
@@ -209,21 +213,31 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
 
-  int kt = next_tile(0);
+  const float c_log2 = a.scale_log2;   // > 0 (checked on the host)
+
+  // ---- double-buffered LDS pipeline over the needed KV tiles -----------------
+  // Iteration i: one barrier (tile i is in LDS; every wave is done with tile
+  // i-1), then dequantise tile i+1 from registers into the other buffer, issue
+  // the global loads of tile i+2, and consume tile i.  The dequantisation and
+  // the matrix work of one iteration are independent, so they interleave.
+  int cur = next_tile(0);
   Staged st;
-  if (kt < nkt) stage_load<K8, V8>(c, kt * KT, tid, st);
+  if (cur < nkt) {
+    stage_load<K8, V8>(c, cur * KT, tid, st);
+    stage_store<K8, V8>(st, cur * KT, n, tid, lds);
+  }
+  int nxt = cur < nkt ? next_tile(cur + 1) : nkt;
+  if (nxt < nkt) stage_load<K8, V8>(c, nxt * KT, tid, st);
+  int bi = 0;
+  while (cur < nkt) {
+    __syncthreads();
+    if (nxt < nkt) stage_store<K8, V8>(st, nxt * KT, n, tid, lds + (bi ^ 1) * LDS_STAGE);
+    const int nn = nxt < nkt ? next_tile(nxt + 1) : nkt;
+    if (nn < nkt) stage_load<K8, V8>(c, nn * KT, tid, st);
 
-  const uint8_t* ks_lds = reinterpret_cast<const uint8_t*>(lds);
-  const uint8_t* vs_lds = reinterpret_cast<const uint8_t*>(lds + LDS_K);
-
-  while (kt < nkt) {
-    const int kt0 = kt * KT;
-    __syncthreads();                          // previous tile fully consumed
-    stage_store<K8, V8>(st, kt0, n, tid, lds);
-    const int kn = next_tile(kt + 1);
-    if (kn < nkt) stage_load<K8, V8>(c, kn * KT, tid, st);
-    __syncthreads();                          // tile visible
-
+    const int kt0 = cur * KT;
+    const uint8_t* ks_lds = reinterpret_cast<const uint8_t*>(lds + bi * LDS_STAGE);
+    const uint8_t* vs_lds = ks_lds + LDS_K;
     const bool wave_needs =
         q0w < n && w_last >= kt0 && mask_keep(a, mb, q0w >> 7, kt0 >> 7);
     if (wave_needs) {
@@ -240,24 +254,30 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
           s[kb] = mfma32x32x16(u4_to_h8(kv), qreg[ks], s[kb]);
         }
       }
-      // ---- scale, mask, online softmax ----
+      // ---- mask, online softmax ----
+      // Scores stay unscaled; the scale is folded into the exponent's FMA.
       const bool need_mask = (kt0 + KT - 1 > q0w) || (kt0 + KT > n) || (q0w + 31 >= n);
-      float mx = NEG_BIG;
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = kt0 + 32 * kb + 8 * (v >> 2) + 4 * hb + (v & 3);
+            if (key > row || key >= n || !row_live) s[kb][v] = -INFINITY;
+          }
+      }
+      float mx = s[0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = s[kb][v] * a.scale_log2;
-          if (need_mask) {
-            const int key = kt0 + 32 * kb + 8 * (v >> 2) + 4 * hb + (v & 3);
-            if (key > row || key >= n || !row_live) x = -INFINITY;
-          }
-          s[kb][v] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, lane_read_f(mx, lane ^ 32));
-      const float mn = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - mn);
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+      mx = fmaxf(mx, lane_read_f(mx, lane ^ 32)) * c_log2;
+      // The running maximum only moves when the tile maximum exceeds it by
+      // more than 8 (log2 units): weights stay below 2^8, exact enough in
+      // fp16, and the accumulator is rescaled only on those tiles.
+      const bool move = mx > m_run + 8.f;
+      const float mn = move ? mx : m_run;
+      const float alpha = move ? fast_exp2(m_run - mn) : 1.f;
       m_run = mn;
       half8 p[4];  // PV k-steps (kb, half)
       float lsum = 0.f;
@@ -267,14 +287,17 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
         for (int hf = 0; hf < 2; ++hf) {
           half8 ph;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ph[e] = (_Float16)fast_exp2(s[kb][8 * hf + e] - mn);
+          for (int e = 0; e < 8; ++e)
+            ph[e] = (_Float16)fast_exp2(fmaf(s[kb][8 * hf + e], c_log2, -mn));
 #pragma unroll
           for (int e = 0; e < 8; e += 2)
-            lsum = __builtin_amdgcn_fdot2(half2v{ph[e], ph[e + 1]}, half2v{(_Float16)1.f, (_Float16)1.f}, lsum, false);
+            lsum = __builtin_amdgcn_fdot2(half2v{ph[e], ph[e + 1]},
+                                          half2v{(_Float16)1.f, (_Float16)1.f}, lsum, false);
           p[2 * kb + hf] = ph;
         }
       l_run = fmaf(l_run, alpha, lsum);
-      if (__any(alpha != 1.f)) {
+      if (__any(move)) {
+        asm volatile("" ::: "memory");   // keep this a real (rare) branch
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db] = o[db] * alpha;
       }
@@ -293,7 +316,9 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
         }
       }
     }
-    kt = kn;
+    cur = nxt;
+    nxt = nn;
+    bi ^= 1;
   }
 
   // ---- epilogue ----
@@ -314,12 +339,19 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
   }
 }
 
+// 1-D grid.  Consecutive workgroup ids go round-robin to the 8 XCDs, so with
+// the KV head as the fastest index every XCD keeps serving the same KV heads
+// (its L2 holds their K/V tiles); query blocks run longest-first.
 template <int R>
 __global__ void __launch_bounds__(NT)
 prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[LDS_K + LDS_V];
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int qblk = a.n_qblk - 1 - (int)blockIdx.x;   // longest rows first
+  __shared__ __attribute__((aligned(16))) char lds[2 * LDS_STAGE];
+  const int H = a.k.H, B = a.k.B;
+  const int id = blockIdx.x;
+  const int g = id % H;
+  const int rest = id / H;
+  const int b = rest % B;
+  const int qblk = a.n_qblk - 1 - rest / B;
   int n = a.lens[b];
   n = n < 0 ? 0 : (n > a.L ? a.L : n);
   const bool k8 = (a.k.is8 >> g) & 1ull, v8 = (a.v.is8 >> g) & 1ull;
@@ -335,7 +367,7 @@ prefill_kernel(PrefillArgs a) {
 }  // namespace
 
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_qblk, a.k.H, a.k.B);
+  const dim3 grid(a.n_qblk * a.k.H * a.k.B);
   switch (a.r) {
     case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(NT), 0, s, a); break;
     case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(NT), 0, s, a); break;

@@ -26,26 +26,41 @@ __device__ __forceinline__ uint32_t h2_to_u32(half2v h) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// A 32-bit constant materialised in a VGPR.  A VALU instruction may read at
+// most one scalar operand (SGPR or literal) on gfx9-family parts, so
+// three-operand bit operations with two constants (v_and_or_b32, v_perm_b32)
+// take one of them from a VGPR; the compiler hoists these moves out of loops.
+__device__ __forceinline__ uint32_t vconst(uint32_t c) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+  return r;
+}
+
 // v_perm_b32: byte i of the result is byte sel_i of the 8-byte value
 // {hi = a, lo = b} (selector 0..3 -> b, 4..7 -> a, 12 -> 0x00).
 __device__ __forceinline__ uint32_t perm_b32(uint32_t a, uint32_t b, uint32_t sel) {
   return __builtin_amdgcn_perm(a, b, sel);
 }
 
+// (x & m) | c in one v_and_or_b32 (m from a VGPR).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  return (x & vconst(m)) | c;
+}
+
 // Two unsigned bytes -> half2 (1024 + c0, 1024 + c1); exact.  `w` holds four
 // bytes; hi_pair selects bytes {2,3} instead of {0,1}.
 __device__ __forceinline__ uint32_t bytes_to_biased_h2(uint32_t w, bool hi_pair) {
-  return perm_b32(0x64646464u, w, hi_pair ? 0x04030402u : 0x04010400u);
+  return perm_b32(vconst(0x64646464u), w, hi_pair ? 0x04030402u : 0x04010400u);
 }
 
 // Two nibbles at bit offsets 4k and 16 + 4k of w -> half2 (1024 + n, 1024 + n').
 __device__ __forceinline__ uint32_t nibbles_to_biased_h2(uint32_t w, int k) {
-  return ((w >> (4 * k)) & 0x000F000Fu) | 0x64006400u;
+  return and_or(k ? (w >> (4 * k)) : w, 0x000F000Fu, 0x64006400u);
 }
 
 // half2 (-(1024 + z), -(1024 + z)) for one byte z (bits 0..7 of zb).
 __device__ __forceinline__ uint32_t neg_biased_zero_h2(uint32_t zb) {
-  return (zb & 0xFFu) * 0x00010001u | 0xE400E400u;
+  return perm_b32(vconst(0xE4E4E4E4u), zb, 0x04000400u);
 }
 
 // DPP moves inside rows of 16 lanes.

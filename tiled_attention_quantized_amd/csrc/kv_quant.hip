@@ -172,10 +172,10 @@ quantize_channel_kernel(QuantArgs a, int p0, int npairs) {
   const int64_t xbase = ((int64_t)b * g.H + h) * a.count;
   if (in0) quantize_group(a.x + ((xbase + T0 - a.start) * g.D + 32 * gi), bits, q0);
   if (in1) quantize_group(a.x + ((xbase + T0 + 1 - a.start) * g.D + 32 * gi), bits, q1);
-  const int rowb = 16 * bits;  // bytes per channel row of a 128-token block
+  const int rowb = 4 * bits;  // bytes per channel row of a 32-token block
   uint8_t* blk = g.codes + (int64_t)b * g.bstride + g.hoff[h] +
-                 (int64_t)(T0 / 128) * g.D * rowb;
-  const int tt = T0 % 128;
+                 (int64_t)(T0 / 32) * g.D * rowb;
+  const int tt = T0 % 32;
 #pragma unroll 4
   for (int i = 0; i < 32; ++i) {
     uint8_t* row = blk + (int64_t)(32 * gi + i) * rowb;
@@ -241,8 +241,8 @@ dequantize_kernel(QuantArgs a) {
       const uint8_t* row = base + (int64_t)T * (g.D * bits / 8);
       c = bits == 8 ? row[d] : ((row[d / 2] >> (4 * (d & 1))) & 15);
     } else {
-      const uint8_t* row = base + ((int64_t)(T / 128) * g.D + d) * (16 * bits);
-      const int tt = T % 128;
+      const uint8_t* row = base + ((int64_t)(T / 32) * g.D + d) * (4 * bits);
+      const int tt = T % 32;
       c = bits == 8 ? row[tt] : ((row[tt / 2] >> (4 * (tt & 1))) & 15);
     }
     const float v = (float)(c - z) * s;   // exact: <= 19 significant bits

@@ -38,6 +38,8 @@ struct DecodeArgs {
   float* ws;             // partials [B][Hq][nchunk][D + 2]
   int32_t Hq, r, max_len, chunk, nchunk;
   float scale_log2;      // softmax scale * log2(e)
+  int32_t nheads;        // KV heads handled by one launch, listed in heads[]
+  uint8_t heads[TAQ_MAX_KV_HEADS];
 };
 
 struct PrefillArgs {
