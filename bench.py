@@ -15,7 +15,7 @@ The JSON line also carries:
                 the stream it runs on) against dense fp16 MFMA peak;
   decode        the long-context decode workload (B=8, Hq=32, Hkv=8, 131072
                 tokens, 2 int8 + 6 int4 KV heads): KV GB/s against HBM peak;
-  cpu_baseline  the fp64 oracle on a bounded sample of the prefill workload.
+  cpu_baseline  the fp64 oracle on the same prefill workload (host cores).
 """
 from __future__ import annotations
 
@@ -33,6 +33,39 @@ sys.path.insert(0, ROOT)
 MFMA_F16_PEAK_TFLOPS = 2500.0     # MI355X dense fp16 MFMA, published
 HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, published
 METRIC = "decode KV GB/s & % HBM peak; prefill TFLOP/s & % MFMA peak"
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "tiled_attention_quantized_amd", "csrc")
+
+
+def source_hash(*names) -> str:
+    """sha256 (first 16 hex digits) of the kernel sources a counter run used."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(summary: str, sources) -> "float | None":
+    """HBM bytes per launch recorded in a profiles/ summary (FETCH_SIZE plus
+    WRITE_SIZE, scaled by the copy-kernel factor), or None when the summary
+    is missing or was taken on different kernel sources."""
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256_16") != source_hash(*sources):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(msg):
@@ -103,7 +136,7 @@ def bench_decode(args, torch, T, W, A):
     nbytes = A.decode_bytes(spec.B, spec.Hq, spec.D, inp.structure.seq_lens,
                             inp.structure.head_bits)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
+    for _ in range(max(args.warmup, 20)):        # let the clocks settle
         T.attn_decode(k, v, q, lens, spec.max_len, out=out, workspace=ws)
     torch.cuda.synchronize()
     iters = max(args.steps, 10)
@@ -130,21 +163,22 @@ def bench_decode(args, torch, T, W, A):
             "value": round(gbs, 1), "unit": "GB/s",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": None}}
+                         "traffic": stored_traffic("decode_split_kernel_decode_128k_mixed.md",
+                                                   ["attn_decode.hip", "device_common.h"])}}
 
 
 def cpu_baseline(inp, A, W):
-    """The oracle as it stands on a bounded sample: 8 of the 32 query heads
-    (the 2 KV groups 0 and 1), all rows, process pool over heads."""
+    """The oracle as it stands on the prefill workload (all 32 query heads, all
+    rows), process pool over heads."""
     from oracle import attention as oa
     from oracle import quant as oq
     spec, st = inp.spec, inp.structure
     workers = oa.default_workers()
-    heads = [(0, h) for h in range(8)]
+    heads = [(0, h) for h in range(spec.Hq)]
     t0 = time.perf_counter()
     kh = np.zeros((1, spec.Hkv, spec.cap, spec.D))
     vh = np.zeros((1, spec.Hkv, spec.cap, spec.D))
-    for g in range(2):
+    for g in range(spec.Hkv):
         kh[0, g] = oq.dequantize(*oq.quantize(inp.k[0, g], int(st.head_bits[g])))
         vh[0, g] = oq.dequantize(*oq.quantize(inp.v[0, g], int(st.head_bits[g])))
     oa.prefill(inp.q, kh, vh, st.seq_lens, heads=heads, workers=workers)
@@ -152,8 +186,8 @@ def cpu_baseline(inp, A, W):
     flops = A.prefill_flops(len(heads), spec.D, st.seq_lens)
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": workers,
             "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "prefill_8k, query heads 0-7 (KV heads 0-1), all 8192 rows; fp64 NumPy, "
-                      f"process pool of {workers} workers, 1 BLAS thread each"}
+            "sample": "prefill_8k in full (32 query heads x 8192 rows, quantisation included); "
+                      f"fp64 NumPy, process pool of {workers} workers, 1 BLAS thread each"}
 
 
 def main():
@@ -164,6 +198,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 1 GiB device copy (for HBM counter calibration) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -177,6 +213,14 @@ def main():
     from workloads import accounting as A
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel()}), flush=True)
+        return
     T.device_check(0)
 
     if args.only == "decode":
@@ -214,7 +258,9 @@ def main():
                    "step": "kv_quantize(K) + kv_quantize(V) + attn_prefill"},
         "roofline": {"bound": "mfma", "achieved": round(kern_tf, 2),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(kern_tf / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(kern_tf / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": stored_traffic("prefill_kernel_prefill_8k.md",
+                                               ["attn_prefill.hip", "device_common.h"]),
                      "kernel": "prefill_kernel<4>", "kernel_ms": round(kern_ms, 4),
                      "flops_per_launch": int(flops)},
         "cpu_baseline": cpu,
