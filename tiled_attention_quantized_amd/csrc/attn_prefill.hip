@@ -13,9 +13,10 @@
 //    r = Hq/Hkv query heads that share one KV head, so every K/V tile is
 //    fetched and dequantised once for r * BQ = 256 (head, row) pairs; wave w
 //    takes head w % r and the 32 rows (w / r) * 32 .. +31;
-//  * the key loop runs in tiles of 64 keys through two LDS stages: while
-//    tile i is consumed, tile i+1 is dequantised into the other stage and
-//    tile i+2 is fetched from HBM into registers (one barrier per tile);
+//  * the key loop runs in tiles of 64 keys through three LDS stages as a
+//    software pipeline: the QK^T MFMAs of tile j+1 interleave with the
+//    softmax of tile j, and the PV MFMAs of tile j with the dequantisation of
+//    tile j+2; tile j+3 is fetched into registers (one barrier per tile);
 //  * both contractions use v_mfma_f32_32x32x16_f16 in transposed form:
 //    S^T = K-hat Q^T (A = K-hat tile from LDS, B = Q held in registers) and
 //    O^T += V-hat^T P^T (A = V-hat^T tile from LDS, B = P straight from the
@@ -147,6 +148,25 @@ __device__ __forceinline__ void stage_store(const Staged& s, int kt0, int n, int
   }
 }
 
+// The same dequantisation as stage_store, one fp16 pair at a time, so it can
+// be interleaved with matrix instructions.  K: pair j (0..7) = channels
+// 16*half + 2j, +1 of the thread's (key, group); V: pair j = keys 16q + 2j, +1
+// of the thread's channel.
+template <bool K8>
+__device__ __forceinline__ uint32_t k_pair(const Staged& s, int j, half2v nz, half2v s2) {
+  const uint32_t c2 = K8 ? bytes_to_biased_h2(s.kc[j >> 1], j & 1) : nib_pair_natural(s.kc[j >> 2], j & 3);
+  return h2_to_u32((u32_to_h2(c2) + nz) * s2);
+}
+template <bool V8>
+__device__ __forceinline__ uint32_t v_pair(const Staged& s, int j, int key0, int n) {
+  const uint32_t c2 = V8 ? bytes_to_biased_h2(s.vc[j >> 1], j & 1) : nib_pair_natural(s.vc[j >> 2], j & 3);
+  const uint32_t nz = perm_b32(vconst(0xE4E4E4E4u), s.vz[j >> 1], (j & 1) ? 0x04030402u : 0x04010400u);
+  uint32_t sc = j < 4 ? s.vs0[j] : s.vs1[j - 4];
+  const int k0 = key0 + 2 * j;
+  sc &= (k0 < n ? 0x0000FFFFu : 0u) | (k0 + 1 < n ? 0xFFFF0000u : 0u);
+  return h2_to_u32((u32_to_h2(c2) + u32_to_h2(nz)) * u32_to_h2(sc));
+}
+
 __device__ __forceinline__ bool mask_keep(const PrefillArgs& a, const uint8_t* mb, int qt, int kt) {
   return mb == nullptr || mb[(int64_t)qt * a.mask_nk + kt] != 0;
 }
@@ -214,63 +234,74 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
     for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
 
   const float c_log2 = a.scale_log2;   // > 0 (checked on the host)
+  const int qt_w = q0w >> 7;            // this wave's 128-row query tile
 
-  // ---- double-buffered LDS pipeline over the needed KV tiles -----------------
-  // Iteration i: one barrier (tile i is in LDS; every wave is done with tile
-  // i-1), then dequantise tile i+1 from registers into the other buffer, issue
-  // the global loads of tile i+2, and consume tile i.  The dequantisation and
-  // the matrix work of one iteration are independent, so they interleave.
-  int cur = next_tile(0);
-  Staged st;
-  if (cur < nkt) {
-    stage_load<K8, V8>(c, cur * KT, tid, st);
-    stage_store<K8, V8>(st, cur * KT, n, tid, lds);
-  }
-  int nxt = cur < nkt ? next_tile(cur + 1) : nkt;
-  if (nxt < nkt) stage_load<K8, V8>(c, nxt * KT, tid, st);
-  int bi = 0;
-  while (cur < nkt) {
-    __syncthreads();
-    if (nxt < nkt) stage_store<K8, V8>(st, nxt * KT, n, tid, lds + (bi ^ 1) * LDS_STAGE);
-    const int nn = nxt < nkt ? next_tile(nxt + 1) : nkt;
-    if (nn < nkt) stage_load<K8, V8>(c, nn * KT, tid, st);
-
-    const int kt0 = cur * KT;
-    const uint8_t* ks_lds = reinterpret_cast<const uint8_t*>(lds + bi * LDS_STAGE);
-    const uint8_t* vs_lds = ks_lds + LDS_K;
-    const bool wave_needs =
-        q0w < n && w_last >= kt0 && mask_keep(a, mb, q0w >> 7, kt0 >> 7);
-    if (wave_needs) {
-      // ---- S^T = K-hat Q^T ----
-      f32x16 s[2];
+  // ---- LDS stage helpers ---------------------------------------------------------
+  auto stage_ptr = [&](int j) -> char* { return lds + (j % 3) * LDS_STAGE; };
+  // S^T = K-hat Q^T for the tile in stage j (16 MFMAs)
+  auto qk = [&](int j, f32x16* S) {
+    const uint8_t* kl = reinterpret_cast<const uint8_t*>(stage_ptr(j));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[kb][v] = 0.f;
+      for (int v = 0; v < 16; ++v) S[kb][v] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const u32x4 kv = *reinterpret_cast<const u32x4*>(
-              ks_lds + (32 * kb + i32) * KS_STRIDE + (16 * ks + 8 * hb) * 2);
-          s[kb] = mfma32x32x16(u4_to_h8(kv), qreg[ks], s[kb]);
-        }
+      for (int ks = 0; ks < 8; ++ks) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(
+            kl + (32 * kb + i32) * KS_STRIDE + (16 * ks + 8 * hb) * 2);
+        S[kb] = mfma32x32x16(u4_to_h8(kv), qreg[ks], S[kb]);
       }
-      // ---- mask, online softmax ----
-      // Scores stay unscaled; the scale is folded into the exponent's FMA.
-      const bool need_mask = (kt0 + KT - 1 > q0w) || (kt0 + KT > n) || (q0w + 31 >= n);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = kt0 + 32 * kb + 8 * (v >> 2) + 4 * hb + (v & 3);
-            if (key > row || key >= n || !row_live) s[kb][v] = -INFINITY;
-          }
-      }
-      float mx = s[0][0];
+    }
+  };
+  // causal / length / dead-row / per-wave mask of tile kt on S (only when needed)
+  auto mask_tile = [&](int kt, f32x16* S) {
+    const int kt0 = kt * KT;
+    const bool keep = mask_keep(a, mb, qt_w, kt0 >> 7);
+    const bool need = !keep || (kt0 + KT - 1 > q0w) || (kt0 + KT > n) || (q0w + 31 >= n);
+    if (need) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+        for (int v = 0; v < 16; ++v) {
+          const int key = kt0 + 32 * kb + 8 * (v >> 2) + 4 * hb + (v & 3);
+          if (!keep || key > row || key >= n || !row_live) S[kb][v] = -INFINITY;
+        }
+    }
+  };
+
+  // ---- software pipeline over the workgroup's KV tiles -------------------------
+  // Tiles t_0, t_1, ... (causal and mask order) go through three LDS stages.
+  // Iteration j (one barrier): the QK^T MFMAs of tile j+1 run interleaved with
+  // the softmax of tile j, then the PV MFMAs of tile j run interleaved with the
+  // dequantisation of tile j+2 into the third stage; tile j+3 is fetched from
+  // HBM into registers.  Every wave walks the same tiles; rows a tile does not
+  // reach are masked, so the loop has no per-wave branches.
+  const int t0_ = next_tile(0);
+  if (t0_ < nkt) {
+    const int t1_ = next_tile(t0_ + 1);
+    const int t2_ = t1_ < nkt ? next_tile(t1_ + 1) : nkt;
+    Staged st;
+    stage_load<K8, V8>(c, t0_ * KT, tid, st);
+    stage_store<K8, V8>(st, t0_ * KT, n, tid, stage_ptr(0));
+    stage_load<K8, V8>(c, (t1_ < nkt ? t1_ : t0_) * KT, tid, st);
+    stage_store<K8, V8>(st, (t1_ < nkt ? t1_ : t0_) * KT, n, tid, stage_ptr(1));
+    stage_load<K8, V8>(c, (t2_ < nkt ? t2_ : t0_) * KT, tid, st);
+    __syncthreads();
+    f32x16 S0[2], S1[2];
+    qk(0, S0);
+    int tj = t0_, tj1 = t1_, tj2 = t2_;
+    int j = 0;
+
+    auto iteration = [&](f32x16* Sc, f32x16* Sn) {
+      const int tj3 = tj2 < nkt ? next_tile(tj2 + 1) : nkt;
+      __syncthreads();
+      mask_tile(tj, Sc);
+      // --- softmax statistics of tile j ---
+      float mx = Sc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, Sc[kb][v]);
       mx = fmaxf(mx, lane_read_f(mx, lane ^ 32)) * c_log2;
       // The running maximum only moves when the tile maximum exceeds it by
       // more than 8 (log2 units): weights stay below 2^8, exact enough in
@@ -279,46 +310,108 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
       const float mn = move ? mx : m_run;
       const float alpha = move ? fast_exp2(m_run - mn) : 1.f;
       m_run = mn;
-      half8 p[4];  // PV k-steps (kb, half)
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          half8 ph;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            ph[e] = (_Float16)fast_exp2(fmaf(s[kb][8 * hf + e], c_log2, -mn));
-#pragma unroll
-          for (int e = 0; e < 8; e += 2)
-            lsum = __builtin_amdgcn_fdot2(half2v{ph[e], ph[e + 1]},
-                                          half2v{(_Float16)1.f, (_Float16)1.f}, lsum, false);
-          p[2 * kb + hf] = ph;
-        }
-      l_run = fmaf(l_run, alpha, lsum);
+      // Rescale before the interleaved blocks, so that no branch separates the
+      // weights of tile j from the PV block that consumes them.
       if (__any(move)) {
         asm volatile("" ::: "memory");   // keep this a real (rare) branch
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db] = o[db] * alpha;
       }
-      // ---- O^T += V-hat^T P^T ----
+
+      // --- QK^T(j+1) interleaved with the weights of tile j ---
+      // MFMA i uses accumulator kb = i % 2 and k-step ks = i / 2; its LDS
+      // operand is read one MFMA ahead; the weights of elements 2i, 2i+1 of
+      // S(j) are computed behind it.  Past the last tile the MFMAs recompute
+      // a resident stage (result unused).
+      const uint8_t* kl = reinterpret_cast<const uint8_t*>(stage_ptr(j + 1));
+      auto kread = [&](int i) -> u32x4 {
+        const int kb = i & 1, ks = i >> 1;
+        return *reinterpret_cast<const u32x4*>(kl + (32 * kb + i32) * KS_STRIDE + (16 * ks + 8 * hb) * 2);
+      };
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint8_t* vr = vs_lds + (32 * db + i32) * VS_STRIDE;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int kb = kk >> 1, hf = kk & 1;
-          const int kbase = 32 * kb + 16 * hf + 4 * hb;
+        for (int v = 0; v < 16; ++v) Sn[kb][v] = 0.f;
+      half8 pk[4];  // PV k-steps (kb, half)
+      float lsum = 0.f;
+      u32x4 kv = kread(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        u32x4 kvn;
+        if (i + 1 < 16) kvn = kread(i + 1);
+        Sn[i & 1] = mfma32x32x16(u4_to_h8(kv), qreg[i >> 1], Sn[i & 1]);
+        const int kb = i >> 3, v = 2 * (i & 7);
+        const _Float16 p0 = (_Float16)fast_exp2(fmaf(Sc[kb][v], c_log2, -mn));
+        const _Float16 p1 = (_Float16)fast_exp2(fmaf(Sc[kb][v + 1], c_log2, -mn));
+        pk[2 * kb + (v >> 3)][v & 7] = p0;
+        pk[2 * kb + (v >> 3)][(v & 7) + 1] = p1;
+        lsum = __builtin_amdgcn_fdot2(half2v{p0, p1}, half2v{(_Float16)1.f, (_Float16)1.f}, lsum, false);
+        if (i + 1 < 16) kv = kvn;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_run = fmaf(l_run, alpha, lsum);
+
+      // --- PV(j) interleaved with the dequantisation of tile j+2 ---
+      // MFMA i uses accumulator db = i % 4 and k-step kk = i / 4; pair i of the
+      // staged tile (K pairs 0..7, then V pairs 0..7) is dequantised behind it.
+      {
+        const uint8_t* vl = reinterpret_cast<const uint8_t*>(stage_ptr(j)) + LDS_K;
+        auto vread = [&](int i) -> u32x4 {
+          const int db = i & 3, kk = i >> 2;
+          const int kbase = 32 * (kk >> 1) + 16 * (kk & 1) + 4 * hb;
+          const uint8_t* vr = vl + (32 * db + i32) * VS_STRIDE;
           const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + kbase * 2);
           const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + (kbase + 8) * 2);
-          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-          o[db] = mfma32x32x16(u4_to_h8(av), p[kk], o[db]);
+          return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        // past the last tile the staged registers repeat a valid tile
+        const int skt0 = (tj2 < nkt ? tj2 : t0_) * KT;
+        char* sdst = stage_ptr(j + 2);
+        const int unit = tid >> 1, khalf = tid & 1;
+        const int kkey = unit >> 2, kgrp = unit & 3;
+        const int vd = tid >> 2, vq = tid & 3;
+        const half2v knz = u32_to_h2(neg_biased_zero_h2(st.kz));
+        const _Float16 ksc = bits_to_half((uint16_t)st.ks);
+        const half2v ks2 = half2v{ksc, ksc};
+        u32x4 ko0, ko1, vo0, vo1;
+        u32x4 av = vread(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          u32x4 avn;
+          if (i + 1 < 16) avn = vread(i + 1);
+          o[i & 3] = mfma32x32x16(u4_to_h8(av), pk[i >> 2], o[i & 3]);
+          if (i < 8) {
+            const uint32_t w = k_pair<K8>(st, i, knz, ks2);
+            if (i < 4) ko0[i] = w; else ko1[i - 4] = w;
+          } else {
+            const uint32_t w = v_pair<V8>(st, i - 8, skt0 + 16 * vq, n);
+            if (i < 12) vo0[i - 8] = w; else vo1[i - 12] = w;
+          }
+          if (i == 7) {
+            u32x4* kd = reinterpret_cast<u32x4*>(sdst + kkey * KS_STRIDE + (32 * kgrp + 16 * khalf) * 2);
+            kd[0] = ko0;
+            kd[1] = ko1;
+          }
+          if (i == 15) {
+            u32x4* vdst = reinterpret_cast<u32x4*>(sdst + LDS_K + vd * VS_STRIDE + 32 * vq);
+            vdst[0] = vo0;
+            vdst[1] = vo1;
+          }
+          if (i + 1 < 16) av = avn;
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
+      stage_load<K8, V8>(c, (tj3 < nkt ? tj3 : t0_) * KT, tid, st);
+      tj = tj1; tj1 = tj2; tj2 = tj3;
+      ++j;
+    };
+
+    while (true) {
+      iteration(S0, S1);
+      if (tj >= nkt) break;
+      iteration(S1, S0);
+      if (tj >= nkt) break;
     }
-    cur = nxt;
-    nxt = nn;
-    bi ^= 1;
   }
 
   // ---- epilogue ----
@@ -339,43 +432,57 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
   }
 }
 
-// 1-D grid.  Consecutive workgroup ids go round-robin to the 8 XCDs, so with
-// the KV head as the fastest index every XCD keeps serving the same KV heads
-// (its L2 holds their K/V tiles); query blocks run longest-first.
-template <int R>
+// One kernel per (K bits, V bits) variant over the KV heads of that variant
+// (a.heads).  1-D grid: consecutive workgroup ids go round-robin to the 8
+// XCDs, so with the KV head as the fastest index every XCD keeps serving the
+// same KV heads (its L2 holds their K/V tiles); query blocks run longest-first.
+template <int R, bool K8, bool V8>
 __global__ void __launch_bounds__(NT)
 prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * LDS_STAGE];
-  const int H = a.k.H, B = a.k.B;
+  __shared__ __attribute__((aligned(16))) char lds[3 * LDS_STAGE];
+  const int H = a.nheads, B = a.k.B;
   const int id = blockIdx.x;
-  const int g = id % H;
+  const int g = a.heads[id % H];
   const int rest = id / H;
   const int b = rest % B;
   const int qblk = a.n_qblk - 1 - rest / B;
   int n = a.lens[b];
   n = n < 0 ? 0 : (n > a.L ? a.L : n);
-  const bool k8 = (a.k.is8 >> g) & 1ull, v8 = (a.v.is8 >> g) & 1ull;
-  if (k8) {
-    if (v8) prefill_body<R, true, true>(a, b, g, qblk, n, lds);
-    else prefill_body<R, true, false>(a, b, g, qblk, n, lds);
-  } else {
-    if (v8) prefill_body<R, false, true>(a, b, g, qblk, n, lds);
-    else prefill_body<R, false, false>(a, b, g, qblk, n, lds);
+  prefill_body<R, K8, V8>(a, b, g, qblk, n, lds);
+}
+
+template <int R>
+hipError_t launch_variants(PrefillArgs a, hipStream_t s) {
+  for (int var = 0; var < 4; ++var) {
+    const bool k8 = var & 2, v8 = var & 1;
+    a.nheads = 0;
+    for (int h = 0; h < a.k.H; ++h)
+      if ((((a.k.is8 >> h) & 1ull) != 0) == k8 && (((a.v.is8 >> h) & 1ull) != 0) == v8)
+        a.heads[a.nheads++] = (uint8_t)h;
+    if (a.nheads == 0) continue;
+    const dim3 grid(a.n_qblk * a.nheads * a.k.B);
+    switch (var) {
+      case 0: hipLaunchKernelGGL((prefill_kernel<R, false, false>), grid, dim3(NT), 0, s, a); break;
+      case 1: hipLaunchKernelGGL((prefill_kernel<R, false, true>), grid, dim3(NT), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((prefill_kernel<R, true, false>), grid, dim3(NT), 0, s, a); break;
+      default: hipLaunchKernelGGL((prefill_kernel<R, true, true>), grid, dim3(NT), 0, s, a); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
 }  // namespace
 
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_qblk * a.k.H * a.k.B);
   switch (a.r) {
-    case 1: hipLaunchKernelGGL(prefill_kernel<1>, grid, dim3(NT), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(prefill_kernel<2>, grid, dim3(NT), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(prefill_kernel<4>, grid, dim3(NT), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(prefill_kernel<8>, grid, dim3(NT), 0, s, a); break;
+    case 1: return launch_variants<1>(a, s);
+    case 2: return launch_variants<2>(a, s);
+    case 4: return launch_variants<4>(a, s);
+    case 8: return launch_variants<8>(a, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace taq

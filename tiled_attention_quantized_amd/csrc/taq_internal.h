@@ -53,6 +53,8 @@ struct PrefillArgs {
   int32_t Hq, r, L;
   int32_t n_qblk;        // query blocks per (b, kv head)
   float scale_log2;
+  int32_t nheads;        // KV heads handled by one launch, listed in heads[]
+  uint8_t heads[TAQ_MAX_KV_HEADS];
 };
 
 hipError_t launch_kv_quantize(const QuantArgs& a, hipStream_t s);
