@@ -193,8 +193,9 @@ def cpu_baseline(inp, A, W):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=2000,
+                    help="untimed steps first (the GPU clock takes about a second to settle)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)

@@ -39,6 +39,18 @@ constexpr int LDS_K = KT * KS_STRIDE;
 constexpr int LDS_V = D * VS_STRIDE;
 constexpr int LDS_STAGE = LDS_K + LDS_V;   // one tile (K-hat and V-hat^T)
 constexpr float NEG_BIG = -1.0e30f;
+#ifndef TAQ_PREFILL_READ_AHEAD
+#define TAQ_PREFILL_READ_AHEAD 3
+#endif
+// LDS operand reads issued this many matrix instructions ahead of their use.
+constexpr int PF_RA = TAQ_PREFILL_READ_AHEAD;
+
+// V-hat^T rows hold the keys of each 16-key group in the order that the PV
+// operand wants them: key 16g + 8a + 4h + c (a, h in {0,1}, c in 0..3) sits at
+// column 16g + 8h + 4a + c.  A lane of row-half h then finds the 8 keys it
+// feeds to one MFMA k-step contiguous, one 16-byte LDS read.  Pair j (keys
+// 2j, 2j+1 of a group) lands in 32-bit column word vslot(j).
+__host__ __device__ constexpr int vslot(int j) { return 4 * ((j >> 1) & 1) + 2 * (j >> 2) + (j & 1); }
 
 // Natural-order nibble pair: channels / keys 2j and 2j+1 of the 8 nibbles in w.
 __device__ __forceinline__ uint32_t nib_pair_natural(uint32_t w, int j) {
@@ -57,6 +69,9 @@ struct Staged {
   u32x4 vs0, vs1;  // V scales of those 16 keys
 };
 
+// Tile-invariant addressing: uniform (scalar) base pointers of this (batch,
+// KV head) and the per-thread offsets of its share of a tile, so a tile load
+// is a scalar base plus a fixed 32-bit lane offset.
 struct TileCtx {
   const uint8_t* kbase;
   const uint8_t* vbase;
@@ -64,39 +79,51 @@ struct TileCtx {
   const uint8_t* kzero;
   const uint16_t* vscale;
   const uint8_t* vzero;
-  int cap;
+  uint32_t k_off;     // K codes, bytes from the tile's first key row
+  uint32_t km_off;    // K scale / zero index from the tile's first key
+  uint32_t v_off;     // V codes, bytes from the tile's first 32-key block
+  uint32_t vm_off;    // V scale / zero index from the tile's first key
 };
 
+// Staging threads: K -> (key = unit / 4, group = unit % 4, half) with unit =
+// tid / 2, 16 channels each; V -> (channel d = tid / 4, quarter q = tid % 4),
+// keys 16q .. 16q+15 of the tile.
 template <bool K8, bool V8>
-__device__ __forceinline__ void stage_load(const TileCtx& c, int kt0, int tid, Staged& s) {
-  // K: thread -> (key, group, half): 16 channels
+__device__ __forceinline__ void tile_ctx_offsets(TileCtx& c, int tid, int cap) {
+  const int unit = tid >> 1, half = tid & 1;
+  const int kkey = unit >> 2, kgrp = unit & 3;
+  c.k_off = (uint32_t)(kkey * (K8 ? D : D / 2) + (K8 ? 32 : 16) * kgrp + (K8 ? 16 : 8) * half);
+  c.km_off = (uint32_t)(kkey * 4 + kgrp);
+  const int d = tid >> 2, q = tid & 3;
+  const int rowb = V8 ? 32 : 16;
+  // key 16q of the tile lies in 32-key block q / 2 at position 16 (q % 2)
+  c.v_off = (uint32_t)(((q >> 1) * D + d) * rowb + (V8 ? 16 : 8) * (q & 1));
+  c.vm_off = (uint32_t)((d >> 5) * cap + 16 * q);
+}
+
+template <bool K8, bool V8>
+__device__ __forceinline__ void stage_load(const TileCtx& c, int kt0, Staged& s) {
   {
-    const int unit = tid >> 1, half = tid & 1;
-    const int key = kt0 + (unit >> 2), grp = unit & 3;
+    const uint8_t* kb = c.kbase + (int64_t)kt0 * (K8 ? D : D / 2);
     if (K8) {
-      s.kc = *reinterpret_cast<const u32x4*>(c.kbase + (int64_t)key * D + 32 * grp + 16 * half);
+      s.kc = *reinterpret_cast<const u32x4*>(kb + c.k_off);
     } else {
-      const u32x2 t = *reinterpret_cast<const u32x2*>(c.kbase + (int64_t)key * (D / 2) + 16 * grp + 8 * half);
+      const u32x2 t = *reinterpret_cast<const u32x2*>(kb + c.k_off);
       s.kc = u32x4{t[0], t[1], 0u, 0u};
     }
-    s.kz = c.kzero[(int64_t)key * 4 + grp];
-    s.ks = c.kscale[(int64_t)key * 4 + grp];
+    s.kz = (c.kzero + (int64_t)kt0 * 4)[c.km_off];
+    s.ks = (c.kscale + (int64_t)kt0 * 4)[c.km_off];
   }
-  // V: thread -> (channel d, quarter q): keys 16q .. 16q+15 of the tile
   {
-    const int d = tid >> 2, q = tid & 3;
-    const int grp = d >> 5;
-    const int key = kt0 + 16 * q;
-    const int blk = key >> 5, kin = key & 31;
-    const uint8_t* row = c.vbase + ((int64_t)blk * D + d) * (V8 ? 32 : 16);
+    const uint8_t* vb = c.vbase + (int64_t)(kt0 >> 5) * D * (V8 ? 32 : 16);
     if (V8) {
-      s.vc = *reinterpret_cast<const u32x4*>(row + kin);
+      s.vc = *reinterpret_cast<const u32x4*>(vb + c.v_off);
     } else {
-      const u32x2 t = *reinterpret_cast<const u32x2*>(row + kin / 2);
+      const u32x2 t = *reinterpret_cast<const u32x2*>(vb + c.v_off);
       s.vc = u32x4{t[0], t[1], 0u, 0u};
     }
-    s.vz = *reinterpret_cast<const u32x4*>(c.vzero + (int64_t)grp * c.cap + kt0 + 16 * q);
-    const u32x4* sp = reinterpret_cast<const u32x4*>(c.vscale + (int64_t)grp * c.cap + kt0 + 16 * q);
+    s.vz = *reinterpret_cast<const u32x4*>(c.vzero + kt0 + c.vm_off);
+    const u32x4* sp = reinterpret_cast<const u32x4*>(c.vscale + kt0 + c.vm_off);
     s.vs0 = sp[0];
     s.vs1 = sp[1];
   }
@@ -140,7 +167,7 @@ __device__ __forceinline__ void stage_store(const Staged& s, int kt0, int n, int
       if (k0 >= n) sc &= 0xFFFF0000u;
       if (k0 + 1 >= n) sc &= 0x0000FFFFu;
       const uint32_t v = h2_to_u32((u32_to_h2(c2) + u32_to_h2(nz)) * u32_to_h2(sc));
-      if (j < 4) o0[j] = v; else o1[j - 4] = v;
+      if (vslot(j) < 4) o0[vslot(j)] = v; else o1[vslot(j) - 4] = v;
     }
     u32x4* dst = reinterpret_cast<u32x4*>(lds + LDS_K + d * VS_STRIDE + 32 * q);
     dst[0] = o0;
@@ -148,23 +175,39 @@ __device__ __forceinline__ void stage_store(const Staged& s, int kt0, int n, int
   }
 }
 
-// The same dequantisation as stage_store, one fp16 pair at a time, so it can
-// be interleaved with matrix instructions.  K: pair j (0..7) = channels
-// 16*half + 2j, +1 of the thread's (key, group); V: pair j = keys 16q + 2j, +1
-// of the thread's channel.
+// The same dequantisation as stage_store, one fp16 pair at a time and split
+// in two steps (code minus zero point, then times the scale) so that the
+// steps of consecutive pairs can be interleaved with matrix instructions.
+// K: pair j (0..7) = channels 16*half + 2j, +1 of the thread's (key, group);
+// V: pair j = keys 16q + 2j, +1 of the thread's channel.
 template <bool K8>
-__device__ __forceinline__ uint32_t k_pair(const Staged& s, int j, half2v nz, half2v s2) {
+__device__ __forceinline__ uint32_t k_centered(const Staged& s, int j, half2v nz) {
   const uint32_t c2 = K8 ? bytes_to_biased_h2(s.kc[j >> 1], j & 1) : nib_pair_natural(s.kc[j >> 2], j & 3);
-  return h2_to_u32((u32_to_h2(c2) + nz) * s2);
+  return h2_to_u32(u32_to_h2(c2) + nz);
 }
 template <bool V8>
-__device__ __forceinline__ uint32_t v_pair(const Staged& s, int j, int key0, int n) {
+__device__ __forceinline__ uint32_t v_centered(const Staged& s, int j) {
   const uint32_t c2 = V8 ? bytes_to_biased_h2(s.vc[j >> 1], j & 1) : nib_pair_natural(s.vc[j >> 2], j & 3);
   const uint32_t nz = perm_b32(vconst(0xE4E4E4E4u), s.vz[j >> 1], (j & 1) ? 0x04030402u : 0x04010400u);
-  uint32_t sc = j < 4 ? s.vs0[j] : s.vs1[j - 4];
-  const int k0 = key0 + 2 * j;
-  sc &= (k0 < n ? 0x0000FFFFu : 0u) | (k0 + 1 < n ? 0xFFFF0000u : 0u);
-  return h2_to_u32((u32_to_h2(c2) + u32_to_h2(nz)) * u32_to_h2(sc));
+  return h2_to_u32(u32_to_h2(c2) + u32_to_h2(nz));
+}
+__device__ __forceinline__ uint32_t v_scales(const Staged& s, int j) {
+  return j < 4 ? s.vs0[j] : s.vs1[j - 4];
+}
+__device__ __forceinline__ uint32_t h2_mul(uint32_t a, uint32_t b) {
+  return h2_to_u32(u32_to_h2(a) * u32_to_h2(b));
+}
+
+// Zero the staged V scales of keys at or beyond n (keys key0 .. key0+15 of
+// this thread), so their V-hat entries are exactly 0 whatever the cache holds
+// past the sequence end.
+__device__ __forceinline__ void zero_tail_scales(Staged& s, int key0, int n) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int k0 = key0 + 2 * j;
+    const uint32_t keep = (k0 < n ? 0x0000FFFFu : 0u) | (k0 + 1 < n ? 0xFFFF0000u : 0u);
+    if (j < 4) s.vs0[j] &= keep; else s.vs1[j - 4] &= keep;
+  }
 }
 
 __device__ __forceinline__ bool mask_keep(const PrefillArgs& a, const uint8_t* mb, int qt, int kt) {
@@ -192,7 +235,7 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
   c.kzero = a.k.zeros + ((int64_t)b * a.k.H + g) * a.k.cap * 4;
   c.vscale = a.v.scales + ((int64_t)b * a.v.H + g) * 4 * (int64_t)a.v.cap;
   c.vzero = a.v.zeros + ((int64_t)b * a.v.H + g) * 4 * (int64_t)a.v.cap;
-  c.cap = a.k.cap;
+  tile_ctx_offsets<K8, V8>(c, tid, a.k.cap);
 
   const uint8_t* mb = a.mask ? a.mask + (int64_t)b * a.mask_sb + (int64_t)g * a.mask_sh : nullptr;
 
@@ -281,11 +324,11 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
     const int t1_ = next_tile(t0_ + 1);
     const int t2_ = t1_ < nkt ? next_tile(t1_ + 1) : nkt;
     Staged st;
-    stage_load<K8, V8>(c, t0_ * KT, tid, st);
+    stage_load<K8, V8>(c, t0_ * KT, st);
     stage_store<K8, V8>(st, t0_ * KT, n, tid, stage_ptr(0));
-    stage_load<K8, V8>(c, (t1_ < nkt ? t1_ : t0_) * KT, tid, st);
+    stage_load<K8, V8>(c, (t1_ < nkt ? t1_ : t0_) * KT, st);
     stage_store<K8, V8>(st, (t1_ < nkt ? t1_ : t0_) * KT, n, tid, stage_ptr(1));
-    stage_load<K8, V8>(c, (t2_ < nkt ? t2_ : t0_) * KT, tid, st);
+    stage_load<K8, V8>(c, (t2_ < nkt ? t2_ : t0_) * KT, st);
     __syncthreads();
     f32x16 S0[2], S1[2];
     qk(0, S0);
@@ -318,9 +361,18 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
         for (int db = 0; db < 4; ++db) o[db] = o[db] * alpha;
       }
 
+      // The staged tile j+2 (past the last tile the staged registers repeat a
+      // valid tile): zero its V scales past the sequence end.  Both rare
+      // branches sit here so no branch splits the interleaved blocks below.
+      const int skt0 = (tj2 < nkt ? tj2 : t0_) * KT;
+      if (skt0 + KT > n) {
+        asm volatile("" ::: "memory");
+        zero_tail_scales(st, skt0 + 16 * (tid & 3), n);
+      }
+
       // --- QK^T(j+1) interleaved with the weights of tile j ---
       // MFMA i uses accumulator kb = i % 2 and k-step ks = i / 2; its LDS
-      // operand is read one MFMA ahead; the weights of elements 2i, 2i+1 of
+      // operand is read PF_RA MFMAs ahead; the weights of elements 2i, 2i+1 of
       // S(j) are computed behind it.  Past the last tile the MFMAs recompute
       // a resident stage (result unused).
       const uint8_t* kl = reinterpret_cast<const uint8_t*>(stage_ptr(j + 1));
@@ -334,19 +386,33 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
         for (int v = 0; v < 16; ++v) Sn[kb][v] = 0.f;
       half8 pk[4];  // PV k-steps (kb, half)
       float lsum = 0.f;
-      u32x4 kv = kread(0);
+      const half2v ones = half2v{(_Float16)1.f, (_Float16)1.f};
+      // Slice i: weights of elements 2i, 2i+1 in fp32; the fp16 rounding and
+      // the row sum of pair i-1 (one slice later, behind the MFMA, so no
+      // dependent instruction follows its producer directly).
+      float e0 = 0.f, e1 = 0.f;
+      u32x4 kv[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        u32x4 kvn;
-        if (i + 1 < 16) kvn = kread(i + 1);
-        Sn[i & 1] = mfma32x32x16(u4_to_h8(kv), qreg[i >> 1], Sn[i & 1]);
-        const int kb = i >> 3, v = 2 * (i & 7);
-        const _Float16 p0 = (_Float16)fast_exp2(fmaf(Sc[kb][v], c_log2, -mn));
-        const _Float16 p1 = (_Float16)fast_exp2(fmaf(Sc[kb][v + 1], c_log2, -mn));
-        pk[2 * kb + (v >> 3)][v & 7] = p0;
-        pk[2 * kb + (v >> 3)][(v & 7) + 1] = p1;
-        lsum = __builtin_amdgcn_fdot2(half2v{p0, p1}, half2v{(_Float16)1.f, (_Float16)1.f}, lsum, false);
-        if (i + 1 < 16) kv = kvn;
+      for (int i = 0; i < PF_RA; ++i) kv[i] = kread(i);
+#pragma unroll
+      for (int i = 0; i <= 16; ++i) {
+        if (i < 16) {
+          if (i + PF_RA < 16) kv[i + PF_RA] = kread(i + PF_RA);
+          Sn[i & 1] = mfma32x32x16(u4_to_h8(kv[i]), qreg[i >> 1], Sn[i & 1]);
+        }
+        half2v hp;
+        if (i > 0) {
+          const int ip = i - 1, kbp = ip >> 3, vp = 2 * (ip & 7);
+          hp = half2v{(_Float16)e0, (_Float16)e1};
+          pk[2 * kbp + (vp >> 3)][vp & 7] = hp[0];
+          pk[2 * kbp + (vp >> 3)][(vp & 7) + 1] = hp[1];
+        }
+        if (i < 16) {
+          const int kb = i >> 3, v = 2 * (i & 7);
+          e0 = fast_exp2(fmaf(Sc[kb][v], c_log2, -mn));
+          e1 = fast_exp2(fmaf(Sc[kb][v + 1], c_log2, -mn));
+        }
+        if (i > 0) lsum = __builtin_amdgcn_fdot2(hp, ones, lsum, false);
         __builtin_amdgcn_sched_barrier(0);
       }
       l_run = fmaf(l_run, alpha, lsum);
@@ -358,14 +424,8 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
         const uint8_t* vl = reinterpret_cast<const uint8_t*>(stage_ptr(j)) + LDS_K;
         auto vread = [&](int i) -> u32x4 {
           const int db = i & 3, kk = i >> 2;
-          const int kbase = 32 * (kk >> 1) + 16 * (kk & 1) + 4 * hb;
-          const uint8_t* vr = vl + (32 * db + i32) * VS_STRIDE;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + kbase * 2);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + (kbase + 8) * 2);
-          return u32x4{lo[0], lo[1], hi[0], hi[1]};
+          return *reinterpret_cast<const u32x4*>(vl + (32 * db + i32) * VS_STRIDE + (16 * kk + 8 * hb) * 2);
         };
-        // past the last tile the staged registers repeat a valid tile
-        const int skt0 = (tj2 < nkt ? tj2 : t0_) * KT;
         char* sdst = stage_ptr(j + 2);
         const int unit = tid >> 1, khalf = tid & 1;
         const int kkey = unit >> 2, kgrp = unit & 3;
@@ -373,35 +433,46 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
         const half2v knz = u32_to_h2(neg_biased_zero_h2(st.kz));
         const _Float16 ksc = bits_to_half((uint16_t)st.ks);
         const half2v ks2 = half2v{ksc, ksc};
+        const uint32_t ks2u = h2_to_u32(ks2);
         u32x4 ko0, ko1, vo0, vo1;
-        u32x4 av = vread(0);
+        u32x4 av[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          u32x4 avn;
-          if (i + 1 < 16) avn = vread(i + 1);
-          o[i & 3] = mfma32x32x16(u4_to_h8(av), pk[i >> 2], o[i & 3]);
-          if (i < 8) {
-            const uint32_t w = k_pair<K8>(st, i, knz, ks2);
-            if (i < 4) ko0[i] = w; else ko1[i - 4] = w;
-          } else {
-            const uint32_t w = v_pair<V8>(st, i - 8, skt0 + 16 * vq, n);
-            if (i < 12) vo0[i - 8] = w; else vo1[i - 12] = w;
+        for (int i = 0; i < PF_RA; ++i) av[i] = vread(i);
+        // Slice i: MFMA i, the scaling of pair i-1 and the centring of pair i.
+        uint32_t cen = 0;
+#pragma unroll
+        for (int i = 0; i <= 16; ++i) {
+          if (i < 16) {
+            if (i + PF_RA < 16) av[i + PF_RA] = vread(i + PF_RA);
+            o[i & 3] = mfma32x32x16(u4_to_h8(av[i]), pk[i >> 2], o[i & 3]);
           }
-          if (i == 7) {
+          if (i > 0) {
+            const int ip = i - 1;
+            if (ip < 8) {
+              const uint32_t w = h2_mul(cen, ks2u);
+              if (ip < 4) ko0[ip] = w; else ko1[ip - 4] = w;
+            } else {
+              const int jv = ip - 8;
+              const uint32_t w = h2_mul(cen, v_scales(st, jv));
+              if (vslot(jv) < 4) vo0[vslot(jv)] = w; else vo1[vslot(jv) - 4] = w;
+            }
+          }
+          if (i < 8) cen = k_centered<K8>(st, i, knz);
+          else if (i < 16) cen = v_centered<V8>(st, i - 8);
+          if (i == 8) {
             u32x4* kd = reinterpret_cast<u32x4*>(sdst + kkey * KS_STRIDE + (32 * kgrp + 16 * khalf) * 2);
             kd[0] = ko0;
             kd[1] = ko1;
           }
-          if (i == 15) {
+          if (i == 16) {
             u32x4* vdst = reinterpret_cast<u32x4*>(sdst + LDS_K + vd * VS_STRIDE + 32 * vq);
             vdst[0] = vo0;
             vdst[1] = vo1;
           }
-          if (i + 1 < 16) av = avn;
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      stage_load<K8, V8>(c, (tj3 < nkt ? tj3 : t0_) * KT, tid, st);
+      stage_load<K8, V8>(c, (tj3 < nkt ? tj3 : t0_) * KT, st);
       tj = tj1; tj1 = tj2; tj2 = tj3;
       ++j;
     };
