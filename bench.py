@@ -262,7 +262,7 @@ def main():
                      "frac": round(kern_tf / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": stored_traffic("prefill_kernel_prefill_8k.md",
                                                ["attn_prefill.hip", "device_common.h"]),
-                     "kernel": "prefill_kernel<4>", "kernel_ms": round(kern_ms, 4),
+                     "kernel": "prefill_kernel<4, true, true>", "kernel_ms": round(kern_ms, 4),
                      "flops_per_launch": int(flops)},
         "cpu_baseline": cpu,
         "decode": dec,
