@@ -135,6 +135,18 @@ size_t taq_kv_meta_count(const taq_kv_cache* cache);
 taq_status taq_kv_quantize(const taq_kv_cache* cache, const void* x_f16,
                            int32_t start, int32_t count, void* stream);
 
+/* Quantise-on-append: the same quantisation, batch entry b's fp16 tokens
+ * x[b][h][0 .. count-1] going to cache positions starts[b] .. starts[b] +
+ * count - 1, so sequences of different lengths each append their next chunk
+ * in one call (the quantisation happens as tokens enter the cache, section
+ * 1.3 of the KV-quantisation page).  starts is a device int32 [B]; positions
+ * outside [0, capacity) are skipped on the device (the host cannot check
+ * device values), and an odd int4 start rewrites only the new token's nibble
+ * of the shared V byte.  Errors: INVALID_ARGUMENT (null pointer, count
+ * outside [0, capacity]), UNSUPPORTED, MISALIGNED (x, starts). */
+taq_status taq_kv_append(const taq_kv_cache* cache, const void* x_f16,
+                         const int32_t* starts, int32_t count, void* stream);
+
 /* Dequantise tokens start .. start+count-1 into out [B][Hkv][count][D] as
  * fp32 (exact) and/or fp16 (round-to-nearest-even of the exact value); either
  * output may be NULL but not both.  A checking aid for the stored format. */
@@ -173,6 +185,24 @@ taq_status taq_attn_prefill(const taq_kv_cache* k_cache,
                             int32_t num_q_heads, const int32_t* seq_lens,
                             int32_t max_seq_len, const taq_tile_mask* mask,
                             float softmax_scale, void* o_f16, void* stream);
+
+/* Chunked prefill against an existing cache: q/o [B][Hq][q_len][D] are the
+ * last q_len positions of each sequence, whose keys and values are already
+ * in the cache (append them first with taq_kv_append), so row i of batch b
+ * sits at position p = seq_lens[b] - q_len + i (bottom-right alignment) and
+ * attends to keys j <= p in tiles the mask keeps, the mask being indexed by
+ * positions; rows with p < 0 are written as zeros.  This is the step of the
+ * multi-turn setting that section 4.2 of the KV-quantisation page discusses:
+ * a new turn reads the quantised history through the same tiled kernel.
+ * q_len must lie in
+ * [0, max_seq_len]; everything else as taq_attn_prefill, which is the case
+ * q_len = max_seq_len with every seq_lens[b] = max_seq_len. */
+taq_status taq_attn_prefill_chunk(const taq_kv_cache* k_cache,
+                                  const taq_kv_cache* v_cache, const void* q_f16,
+                                  int32_t num_q_heads, int32_t q_len,
+                                  const int32_t* seq_lens, int32_t max_seq_len,
+                                  const taq_tile_mask* mask, float softmax_scale,
+                                  void* o_f16, void* stream);
 
 /* Test hook: when `arch` is non-NULL, taq_device_check compares this string
  * instead of the device's architecture name (NULL restores the real check). */

@@ -15,7 +15,10 @@ For batch b, query head h, KV head g = h // (Hq / Hkv) and query row i:
     o_i  = sum_{j in A} exp(s_j - M) v_hat[j] / sum_{j in A} exp(s_j - M),
            M = max_{j in A} s_j;  o_i = 0 when A(i) is empty.
 
-Prefill: pos(i) = i and rows i >= n_b are padding (A(i) empty).  Decode: one
+Prefill: pos(i) = i and rows i >= n_b are padding (A(i) empty).  Chunked
+prefill (a chunk of Lq new rows whose keys are already appended to the cache):
+pos(i) = n_b - Lq + i, the last Lq positions of the sequence (rows with
+pos < 0 are padding); the tile mask is indexed by positions.  Decode: one
 query row per head that attends to every cached key, so pos = n_b - 1 and the
 mask has a single query-tile row per batch entry.
 
@@ -62,7 +65,7 @@ def _rows_one_head(q_rows, row_idx, k, v, n, mask_b, tau, causal):
             allowed &= j[None, :] <= ii[:, None]
             allowed &= (ii < n)[:, None]
         if mask_b is not None:
-            qt = ii // TILE if causal else np.zeros_like(ii)
+            qt = np.maximum(ii, 0) // TILE if causal else np.zeros_like(ii)
             allowed &= mask_b[qt[:, None], (j // TILE)[None, :]].astype(bool)
         s = np.where(allowed, s, -np.inf)
         m = s.max(axis=1)
@@ -96,7 +99,8 @@ def _job(args):
         q_rows = g["q"][b, h][rows].astype(np.float64)
     else:
         q_rows = g["q"][b, h][None, :].astype(np.float64)
-    return _rows_one_head(q_rows, np.asarray(rows), g["k"][b, kvh], g["v"][b, kvh],
+    pos = np.asarray(rows) + int(g.get("qoff", np.zeros(b + 1, dtype=np.int64))[b])
+    return _rows_one_head(q_rows, pos, g["k"][b, kvh], g["v"][b, kvh],
                           int(g["lens"][b]), _mask_for(g["mask"], b), g["tau"],
                           g["causal"])
 
@@ -131,6 +135,30 @@ def prefill(q, k_hat, v_hat, seq_lens, mask=None, scale=None, rows=None,
     heads = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else heads
     payload = dict(q=q, k=k_hat, v=v_hat, lens=np.asarray(seq_lens), mask=mask,
                    tau=tau, r=Hq // Hkv, causal=True)
+    res = _run([(b, h, rows) for b, h in heads], payload, workers)
+    out = np.zeros((B, Hq, len(rows), D), dtype=np.float64)
+    for (b, h), o in zip(heads, res):
+        out[b, h] = o
+    return out
+
+
+def prefill_chunk(q, k_hat, v_hat, seq_lens, mask=None, scale=None, rows=None,
+                  heads=None, workers=1):
+    """Chunked prefill: q fp16 [B][Hq][Lq][D] holds the last Lq positions of
+    each sequence, whose keys and values are already in the cache, so row i of
+    batch b sits at position seq_lens[b] - Lq + i (bottom-right alignment);
+    rows at negative positions are padding (zero).  mask: None, [nq][nk] or
+    [B][nq][nk] over positions.  Returns fp64 [B][Hq][R][D]."""
+    B, Hq, Lq, D = q.shape
+    Hkv = k_hat.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    tau = (1.0 / math.sqrt(D)) if scale is None else float(scale)
+    rows = np.arange(Lq) if rows is None else np.asarray(rows)
+    heads = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else heads
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    payload = dict(q=q, k=k_hat, v=v_hat, lens=lens, mask=mask, tau=tau,
+                   r=Hq // Hkv, causal=True, qoff=lens - Lq)
     res = _run([(b, h, rows) for b, h in heads], payload, workers)
     out = np.zeros((B, Hq, len(rows), D), dtype=np.float64)
     for (b, h), o in zip(heads, res):

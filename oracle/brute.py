@@ -65,6 +65,37 @@ def prefill(q, k, v, seq_lens, Hq, Hkv, mask=None, tau=None, tile=128):
     return out
 
 
+def prefill_chunk(q, k, v, seq_lens, Hq, Hkv, mask=None, tau=None, tile=128):
+    """Chunk of Lq = len(q[b][h]) query rows at positions n_b - Lq + i (keys
+    already in k/v); mask[qt][kt] over positions or None.  Returns
+    out[b][h][i][c]."""
+    B = len(q)
+    D = len(q[0][0][0])
+    tau = 1.0 / math.sqrt(D) if tau is None else tau
+    r = Hq // Hkv
+    out = []
+    for b in range(B):
+        n = int(seq_lens[b])
+        ob = []
+        for h in range(Hq):
+            g = h // r
+            qs = [[float(x) for x in row] for row in q[b][h]]
+            ks = [[float(x) for x in row] for row in k[b][g]]
+            vs = [[float(x) for x in row] for row in v[b][g]]
+            off = n - len(qs)
+
+            def allowed(i, j, off=off):
+                p = off + i
+                if p < 0 or j > p:
+                    return False
+                if mask is not None and not mask[p // tile][j // tile]:
+                    return False
+                return True
+            ob.append(attention_rows(qs, ks, vs, n, allowed, tau))
+        out.append(ob)
+    return out
+
+
 def decode(q, k, v, seq_lens, Hq, Hkv, mask=None, tau=None, tile=128):
     """q[b][h][c]; mask[b][kt] or None.  Returns out[b][h][c]."""
     B = len(q)

@@ -154,3 +154,42 @@ def test_arch_override_rejects_other_gpus():
         assert L.taq_device_check(0) == OK
     finally:
         L.taq_debug_set_arch_override(None)
+
+
+def chunk_call(k=None, v=None, hq=8, q_len=64, max_len=200, mask=None, q=FAKE, o=FAKE,
+               lens=FAKE, scale=0.0):
+    k = k or cache(B=1, H=2, cap=256, bits=(8, 8), layout=0)
+    v = v or cache(B=1, H=2, cap=256, bits=(8, 8), layout=1)
+    m = ctypes.byref(mask) if mask is not None else None
+    return status_of(T.lib().taq_attn_prefill_chunk(ctypes.byref(k), ctypes.byref(v), q, hq,
+                                                    q_len, lens, max_len, m, scale, o, None))
+
+
+def test_chunk_prefill_rejects():
+    # the checks shared with taq_attn_prefill
+    assert chunk_call(hq=7)[0] == INVALID
+    assert chunk_call(hq=6)[0] == UNSUPPORTED
+    assert chunk_call(max_len=300)[0] == INVALID
+    assert chunk_call(q=0)[0] == INVALID
+    assert chunk_call(lens=FAKE + 4)[0] == MISALIGNED
+    assert chunk_call(scale=-1.0)[0] == UNSUPPORTED
+    assert chunk_call(mask=T._Mask(FAKE, 128, 2, 1, 0, 0))[0] == INVALID
+    # its own: q_len within [0, max_seq_len]
+    assert chunk_call(q_len=201)[0] == INVALID
+    assert chunk_call(q_len=-1)[0] == INVALID
+    if not os.path.exists("/dev/kfd"):
+        assert chunk_call(q_len=0)[0] == HIP          # valid: stops at the device query
+        assert chunk_call(q_len=200)[0] == HIP
+
+
+def test_kv_append_rejects():
+    L = T.lib()
+    d = cache()
+    assert L.taq_kv_append(ctypes.byref(d), 0, FAKE, 4, None) == INVALID
+    assert L.taq_kv_append(ctypes.byref(d), FAKE, 0, 4, None) == INVALID
+    assert L.taq_kv_append(ctypes.byref(d), FAKE, FAKE + 4, 4, None) == MISALIGNED
+    assert L.taq_kv_append(ctypes.byref(d), FAKE, FAKE, -1, None) == INVALID
+    assert L.taq_kv_append(ctypes.byref(d), FAKE, FAKE, 257, None) == INVALID
+    assert L.taq_kv_append(ctypes.byref(cache(bits=(3, 4))), FAKE, FAKE, 4, None) == UNSUPPORTED
+    if not os.path.exists("/dev/kfd"):
+        assert L.taq_kv_append(ctypes.byref(d), FAKE, FAKE, 256, None) == HIP

@@ -172,3 +172,52 @@ def test_worker_pool_gives_same_result():
     o1 = att.prefill(q, k, v, [200])
     o2 = att.prefill(q, k, v, [200], workers=3)
     np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+
+
+# --- chunked prefill (rows at positions n_b - Lq + i) --------------------------
+
+def test_chunk_matches_brute_force_with_mask_and_padding():
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, Lq, cap, D = 3, 4, 2, 40, 300, 16
+    q = _rand(rng, (B, Hq, Lq, D))
+    k = _rand(rng, (B, Hkv, cap, D)).astype(np.float64)
+    v = _rand(rng, (B, Hkv, cap, D)).astype(np.float64)
+    lens = np.array([300, 150, 25])          # batch 2: 15 padding rows
+    mask = np.tril(np.ones((3, 3), np.uint8))
+    mask[2, 0] = 0
+    mask[1, 1] = 0                           # the chunk of batch 1 straddles tiles 0 / 1
+    ours = att.prefill_chunk(q, k, v, lens, mask=mask)
+    ref = np.array(brute.prefill_chunk(q.astype(np.float64), k, v, lens, Hq, Hkv, mask=mask))
+    np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-12)
+    assert not ours[2, :, :15].any() and ours[2, :, 15:].any()
+
+
+def test_chunk_equals_the_same_rows_of_a_full_prefill():
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, L, D, Lq = 2, 4, 1, 520, 32, 72
+    qf = _rand(rng, (B, Hq, L, D))
+    k = _rand(rng, (B, Hkv, L, D)).astype(np.float64)
+    v = _rand(rng, (B, Hkv, L, D)).astype(np.float64)
+    lens = np.array([520, 333])
+    mask = np.ones((5, 5), np.uint8)
+    mask[3, 1] = 0
+    mask[4, 2] = 0
+    full = att.prefill(qf, k, v, lens, mask=mask)
+    for b in range(B):
+        n = int(lens[b])
+        qc = np.zeros((B, Hq, Lq, D), np.float16)
+        qc[b] = qf[b, :, n - Lq:n]
+        got = att.prefill_chunk(qc, k, v, lens, mask=mask, heads=[(b, h) for h in range(Hq)])
+        np.testing.assert_allclose(got[b], full[b, :, n - Lq:n], rtol=0, atol=1e-12)
+
+
+def test_chunk_of_one_row_is_decode():
+    rng = np.random.default_rng(13)
+    B, Hq, Hkv, cap, D = 3, 8, 2, 400, 16
+    q = _rand(rng, (B, Hq, D))
+    k = _rand(rng, (B, Hkv, cap, D)).astype(np.float64)
+    v = _rand(rng, (B, Hkv, cap, D)).astype(np.float64)
+    lens = np.array([400, 1, 257])
+    dec = att.decode(q, k, v, lens)
+    chk = att.prefill_chunk(q[:, :, None, :], k, v, lens)
+    np.testing.assert_allclose(chk[:, :, 0], dec, rtol=0, atol=1e-13)

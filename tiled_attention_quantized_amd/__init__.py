@@ -30,7 +30,8 @@ STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "MISALIGNED",
 EXPORTS = ("taq_last_error", "taq_abi_version", "taq_device_check",
            "taq_kv_codes_bytes", "taq_kv_meta_count", "taq_kv_quantize",
            "taq_kv_dequantize", "taq_attn_decode_workspace_bytes",
-           "taq_attn_decode", "taq_attn_prefill", "taq_debug_set_arch_override")
+           "taq_attn_decode", "taq_attn_prefill", "taq_debug_set_arch_override",
+           "taq_kv_append", "taq_attn_prefill_chunk")
 
 
 class TaqError(RuntimeError):
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
         "taq_attn_decode": (ctypes.c_int, [CP, CP, P, I32, P, I32, MP, F, P, P, SZ, P]),
         "taq_attn_prefill": (ctypes.c_int, [CP, CP, P, I32, P, I32, MP, F, P, P]),
         "taq_debug_set_arch_override": (None, [ctypes.c_char_p]),
+        "taq_kv_append": (ctypes.c_int, [CP, P, P, I32, P]),
+        "taq_attn_prefill_chunk": (ctypes.c_int, [CP, CP, P, I32, I32, P, I32, MP, F, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -173,6 +176,21 @@ def kv_quantize(cache: KVCache, x, start: int = 0) -> None:
     _check(lib().taq_kv_quantize(ctypes.byref(d), _ptr(x), start, S, _stream(x.device)))
 
 
+def kv_append(cache: KVCache, x, starts) -> None:
+    """Quantise fp16 x [B][Hkv][S][D] into positions starts[b] .. starts[b]+S-1
+    of each batch entry b; starts is a device int32 [B] tensor."""
+    import torch
+    if x.dtype != torch.float16 or not x.is_contiguous() or x.dim() != 4:
+        raise ValueError("x must be a contiguous fp16 [B][Hkv][S][D] tensor")
+    B, H, S, D = x.shape
+    if (B, H, D) != (cache.batch, cache.num_kv_heads, cache.head_dim):
+        raise ValueError("x shape does not match the cache")
+    if starts.dtype != torch.int32 or starts.numel() != B or not starts.is_contiguous():
+        raise ValueError("starts must be a contiguous int32 [B] tensor")
+    d = cache.desc()
+    _check(lib().taq_kv_append(ctypes.byref(d), _ptr(x), _ptr(starts), S, _stream(x.device)))
+
+
 def kv_dequantize(cache: KVCache, start: int, count: int, f32: bool = True,
                   f16: bool = False):
     """Dequantised tokens [B][Hkv][count][D] as (fp32 or None, fp16 or None)."""
@@ -227,4 +245,23 @@ def attn_prefill(k: KVCache, v: KVCache, q, seq_lens, mask: Optional[TileMask] =
                                   _ptr(seq_lens), L,
                                   ctypes.byref(md) if md is not None else None,
                                   softmax_scale, _ptr(out), _stream(q.device)))
+    return out
+
+
+def attn_prefill_chunk(k: KVCache, v: KVCache, q, seq_lens, max_seq_len: int,
+                       mask: Optional[TileMask] = None, softmax_scale: float = 0.0,
+                       out=None):
+    """Chunked prefill: q fp16 [B][Hq][Lq][D] holds the last Lq positions of each
+    sequence (already appended to the cache); row i of batch b sits at
+    position seq_lens[b] - Lq + i."""
+    import torch
+    B, Hq, Lq, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    kd, vd = k.desc(), v.desc()
+    md = mask.desc() if mask is not None else None
+    _check(lib().taq_attn_prefill_chunk(ctypes.byref(kd), ctypes.byref(vd), _ptr(q), Hq, Lq,
+                                        _ptr(seq_lens), max_seq_len,
+                                        ctypes.byref(md) if md is not None else None,
+                                        softmax_scale, _ptr(out), _stream(q.device)))
     return out

@@ -276,12 +276,20 @@ taq_status taq_attn_decode(const taq_kv_cache* k, const taq_kv_cache* v, const v
   return e == hipSuccess ? TAQ_OK : hip_fail(e, "attn_decode launch");
 }
 
-taq_status taq_attn_prefill(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
-                            int32_t hq, const int32_t* lens, int32_t max_len,
-                            const taq_tile_mask* mask, float softmax_scale, void* o,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of taq_attn_prefill (q_len = max_len, chunk = false) and
+// taq_attn_prefill_chunk.
+taq_status prefill_common(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
+                          int32_t hq, int32_t q_len, bool chunk, const int32_t* lens,
+                          int32_t max_len, const taq_tile_mask* mask, float softmax_scale,
+                          void* o, void* stream) {
   taq_status st = check_pair(k, v, hq, max_len);
   if (st) return st;
+  if (q_len < 0 || q_len > max_len)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "q_len %d outside [0, max_seq_len %d]", q_len, max_len);
   if (!q || !o || !lens) return fail(TAQ_ERR_INVALID_ARGUMENT, "null q, o or seq_lens");
   if (!aligned16(q) || !aligned16(o) || !aligned16(lens))
     return fail(TAQ_ERR_MISALIGNED, "q, o and seq_lens must be 16-byte aligned");
@@ -294,7 +302,7 @@ taq_status taq_attn_prefill(const taq_kv_cache* k, const taq_kv_cache* v, const 
   if (st) return st;
   st = device_ok();
   if (st) return st;
-  if (max_len == 0) return TAQ_OK;
+  if (max_len == 0 || q_len == 0) return TAQ_OK;
   taq::PrefillArgs a;
   std::memset(&a, 0, sizeof(a));
   a.k = geom_of(k);
@@ -312,11 +320,56 @@ taq_status taq_attn_prefill(const taq_kv_cache* k, const taq_kv_cache* v, const 
   a.Hq = hq;
   a.r = hq / k->num_kv_heads;
   a.L = max_len;
+  a.Lq = q_len;
+  a.chunk = chunk ? 1 : 0;
   const int bq = 256 / a.r;
-  a.n_qblk = (max_len + bq - 1) / bq;
+  a.n_qblk = (q_len + bq - 1) / bq;
   a.scale_log2 = scale_log2_of(softmax_scale, 128);
   hipError_t e = taq::launch_attn_prefill(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TAQ_OK : hip_fail(e, "attn_prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+taq_status taq_attn_prefill(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
+                            int32_t hq, const int32_t* lens, int32_t max_len,
+                            const taq_tile_mask* mask, float softmax_scale, void* o,
+                            void* stream) {
+  return prefill_common(k, v, q, hq, max_len, false, lens, max_len, mask, softmax_scale, o,
+                        stream);
+}
+
+taq_status taq_attn_prefill_chunk(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
+                                  int32_t hq, int32_t q_len, const int32_t* lens,
+                                  int32_t max_len, const taq_tile_mask* mask,
+                                  float softmax_scale, void* o, void* stream) {
+  return prefill_common(k, v, q, hq, q_len, true, lens, max_len, mask, softmax_scale, o,
+                        stream);
+}
+
+taq_status taq_kv_append(const taq_kv_cache* c, const void* x, const int32_t* starts,
+                         int32_t count, void* stream) {
+  taq_status st = check_cache(c, "cache", -1, false);
+  if (st) return st;
+  if (!x || !starts) return fail(TAQ_ERR_INVALID_ARGUMENT, "x or starts: null");
+  if (!aligned16(x) || !aligned16(starts))
+    return fail(TAQ_ERR_MISALIGNED, "x and starts must be 16-byte aligned");
+  if (count < 0 || count > c->capacity)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "count %d outside [0, capacity %d]", count,
+                c->capacity);
+  st = device_ok();
+  if (st) return st;
+  taq::QuantArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.c = geom_of(c);
+  a.x = static_cast<const uint16_t*>(x);
+  a.start = 0;
+  a.count = count;
+  a.starts = starts;
+  hipError_t e = taq::launch_kv_quantize(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TAQ_OK : hip_fail(e, "kv_append launch");
 }
 
 }  // extern "C"

@@ -225,8 +225,15 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
   const int hq = g * R + hl;
   const int q0 = qblk * BQ;
   const int q0w = q0 + 32 * rblk;
-  const int row = q0w + i32;
-  const bool row_live = row < n;
+  const int row = q0w + i32;             // row of q / o
+  // Position of row 0 in the sequence: 0 for a whole-sequence prefill; for a
+  // chunk of Lq new rows whose keys are already in the cache, n - Lq (rows
+  // at negative positions are padding).  Causality and the tile mask work
+  // on positions.
+  const int qoff = a.chunk ? n - a.Lq : 0;
+  const int pos = row + qoff;
+  const int p0w = q0w + qoff;            // position of the wave's first row
+  const bool row_live = row < a.Lq && pos >= 0 && pos < n;
 
   TileCtx c;
   c.kbase = a.k.codes + (int64_t)b * a.k.bstride + a.k.hoff[g];
@@ -242,21 +249,20 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
   // Q row of this lane (B operand of S^T): channels 16ks + 8hb .. +7
   half8 qreg[8];
   {
-    const uint16_t* qp = a.q + (((int64_t)b * a.Hq + hq) * a.L + row) * D + 8 * hb;
+    const uint16_t* qp = a.q + (((int64_t)b * a.Hq + hq) * a.Lq + row) * D + 8 * hb;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < a.L) v = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+      if (row < a.Lq) v = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
       qreg[ks] = u4_to_h8(v);
     }
   }
 
   // rows of the workgroup that can see any key, and key range
-  const int wg_last = min(q0 + BQ, n) - 1;            // last live row of the WG
-  const int w_last = min(q0w + 31, n - 1);            // last live row of this wave
-                                                      // (meaningful when q0w < n)
+  // last live position of the workgroup
+  const int wg_last = min(min(q0 + BQ, a.Lq) - 1 + qoff, n - 1);
   const int nkt = wg_last >= 0 ? wg_last / KT + 1 : 0;
-  const int qt_first = q0 >> 7, qt_last = wg_last >= 0 ? (wg_last >> 7) : -1;
+  const int qt_first = max(q0 + qoff, 0) >> 7, qt_last = wg_last >= 0 ? (wg_last >> 7) : -1;
 
   auto wg_needs = [&](int kt) -> bool {
     const int kt128 = (kt * KT) >> 7;
@@ -277,7 +283,9 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
     for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
 
   const float c_log2 = a.scale_log2;   // > 0 (checked on the host)
-  const int qt_w = q0w >> 7;            // this wave's 128-row query tile
+  // this lane's 128-row query tile (clamped, so lanes past the last row never
+  // index beyond the mask's ceil(max_seq_len / 128) tile rows)
+  const int qt_l = min(max(pos, 0), a.L - 1) >> 7;
 
   // ---- LDS stage helpers ---------------------------------------------------------
   auto stage_ptr = [&](int j) -> char* { return lds + (j % 3) * LDS_STAGE; };
@@ -299,15 +307,16 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
   // causal / length / dead-row / per-wave mask of tile kt on S (only when needed)
   auto mask_tile = [&](int kt, f32x16* S) {
     const int kt0 = kt * KT;
-    const bool keep = mask_keep(a, mb, qt_w, kt0 >> 7);
-    const bool need = !keep || (kt0 + KT - 1 > q0w) || (kt0 + KT > n) || (q0w + 31 >= n);
+    const bool keep = mask_keep(a, mb, qt_l, kt0 >> 7);
+    const bool need = __any(!keep) || (kt0 + KT - 1 > p0w) || (kt0 + KT > n) || (p0w + 31 >= n) ||
+                      (p0w < 0) || (q0w + 31 >= a.Lq);
     if (need) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kt0 + 32 * kb + 8 * (v >> 2) + 4 * hb + (v & 3);
-          if (!keep || key > row || key >= n || !row_live) S[kb][v] = -INFINITY;
+          if (!keep || key > pos || key >= n || !row_live) S[kb][v] = -INFINITY;
         }
     }
   };
@@ -488,8 +497,8 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
   // ---- epilogue ----
   const float lt = l_run + lane_read_f(l_run, lane ^ 32);
   const float inv = (row_live && lt > 0.f) ? 1.f / lt : 0.f;
-  if (row < a.L) {
-    uint16_t* op = a.o + (((int64_t)b * a.Hq + hq) * a.L + row) * D;
+  if (row < a.Lq) {
+    uint16_t* op = a.o + (((int64_t)b * a.Hq + hq) * a.Lq + row) * D;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll

@@ -118,10 +118,12 @@ quantize_token_kernel(QuantArgs a) {
   const int h = (int)(rest % g.H);
   const int b = (int)(rest / g.H);
   const int bits = head_bits(g, h);
+  // append: per-batch start, positions outside the capacity are skipped
+  const int T = (a.starts ? a.starts[b] : a.start) + t;
+  if (T < 0 || T >= g.cap) return;
   GroupQ q;
   quantize_group(a.x + ((((int64_t)b * g.H + h) * a.count + t) * g.D + 32 * gi),
                  bits, q);
-  const int T = a.start + t;
   uint8_t* row = g.codes + (int64_t)b * g.bstride + g.hoff[h] +
                  (int64_t)T * (g.D * bits / 8) + gi * 4 * bits;
   if (bits == 8) {
@@ -158,20 +160,23 @@ quantize_channel_kernel(QuantArgs a, int p0, int npairs) {
   const int64_t total = (int64_t)g.B * g.H * G * npairs;
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (id >= total) return;
-  const int p = p0 + (int)(id % npairs);
   int64_t rest = id / npairs;
   const int gi = (int)(rest % G);
   rest /= G;
   const int h = (int)(rest % g.H);
   const int b = (int)(rest / g.H);
+  // append: per-batch start; the pair index is relative to the start's pair
+  const int start = a.starts ? a.starts[b] : a.start;
+  const int p = (a.starts ? (start >> 1) : p0) + (int)(id % npairs);
   const int bits = head_bits(g, h);
   const int T0 = 2 * p;
-  const bool in0 = T0 >= a.start && T0 < a.start + a.count;
-  const bool in1 = T0 + 1 >= a.start && T0 + 1 < a.start + a.count;
+  const bool in0 = T0 >= start && T0 < start + a.count && T0 >= 0 && T0 < g.cap;
+  const bool in1 = T0 + 1 >= start && T0 + 1 < start + a.count && T0 + 1 >= 0 && T0 + 1 < g.cap;
+  if (!in0 && !in1) return;
   GroupQ q0, q1;
   const int64_t xbase = ((int64_t)b * g.H + h) * a.count;
-  if (in0) quantize_group(a.x + ((xbase + T0 - a.start) * g.D + 32 * gi), bits, q0);
-  if (in1) quantize_group(a.x + ((xbase + T0 + 1 - a.start) * g.D + 32 * gi), bits, q1);
+  if (in0) quantize_group(a.x + ((xbase + T0 - start) * g.D + 32 * gi), bits, q0);
+  if (in1) quantize_group(a.x + ((xbase + T0 + 1 - start) * g.D + 32 * gi), bits, q1);
   const int rowb = 4 * bits;  // bytes per channel row of a 32-token block
   uint8_t* blk = g.codes + (int64_t)b * g.bstride + g.hoff[h] +
                  (int64_t)(T0 / 32) * g.D * rowb;
@@ -262,9 +267,9 @@ hipError_t launch_kv_quantize(const QuantArgs& a, hipStream_t s) {
     const int64_t n = (int64_t)a.c.B * a.c.H * a.count * G;
     hipLaunchKernelGGL(quantize_token_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, a);
   } else {
-    const int p0 = a.start / 2;
-    const int p1 = (a.start + a.count - 1) / 2;
-    const int np = p1 - p0 + 1;
+    // per-batch starts: up to count / 2 + 1 pairs from each start's pair
+    const int p0 = a.starts ? 0 : a.start / 2;
+    const int np = a.starts ? a.count / 2 + 1 : (a.start + a.count - 1) / 2 - p0 + 1;
     const int64_t n = (int64_t)a.c.B * a.c.H * G * np;
     hipLaunchKernelGGL(quantize_channel_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s,
                        a, p0, np);

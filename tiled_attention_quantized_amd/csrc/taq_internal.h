@@ -23,6 +23,7 @@ struct QuantArgs {
   CacheGeom c;
   const uint16_t* x;     // fp16 [B][H][count][D]
   int32_t start, count;
+  const int32_t* starts; // device [B] per-batch start (append), or null: start
   float* out32;          // dequantise outputs (either may be null)
   uint16_t* out16;
 };
@@ -50,8 +51,10 @@ struct PrefillArgs {
   const uint8_t* mask;
   int64_t mask_sb, mask_sh;
   int32_t mask_nq, mask_nk;
-  int32_t Hq, r, L;
-  int32_t n_qblk;        // query blocks per (b, kv head)
+  int32_t Hq, r, L;      // L: max_seq_len (bound on the sequence lengths)
+  int32_t Lq;            // rows of q / o (L for a whole-sequence prefill)
+  int32_t chunk;         // nonzero: row i sits at position n_b - Lq + i
+  int32_t n_qblk;        // query blocks per (b, kv head) over Lq rows
   float scale_log2;
   int32_t nheads;        // KV heads handled by one launch, listed in heads[]
   uint8_t heads[TAQ_MAX_KV_HEADS];
