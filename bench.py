@@ -167,6 +167,105 @@ def bench_decode(args, torch, T, W, A):
                                                    ["attn_decode.hip", "device_common.h"])}}
 
 
+def _median_ms(torch, fn, reps, settle_s=2.0):
+    """Median / p10 / p90 of `reps` calls timed with HIP events on the current
+    stream, after `settle_s` seconds of untimed calls."""
+    t_end = time.time() + settle_s
+    while time.time() < t_end:
+        fn()
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return (float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90)))
+
+
+def bench_extras(which, torch, T, W, A):
+    """Timings of the paths beside the headline step, one JSON line each:
+    sparse   attn_prefill on the 128K workload with its seeded 25% tile mask;
+    maskgen  tile_mask_generate (skip 250 per mille) on the same Q and K;
+    chunk    a 512-row chunk against 8192 cached tokens (Hq 32, Hkv 8, int8),
+             alone and with the two kv_append calls of the new tokens."""
+    if {"sparse", "maskgen"} & set(which):
+        spec = W.WORKLOADS["prefill_128k_sparse"]
+        log(f"generating {spec.name}")
+        inp = W.make_inputs(spec)
+        st = inp.structure
+        k, v = make_caches(T, inp, torch)
+        T.kv_quantize(k, torch.from_numpy(inp.k).cuda(), 0)
+        T.kv_quantize(v, torch.from_numpy(inp.v).cuda(), 0)
+        q = torch.from_numpy(inp.q).cuda()
+        lens = torch.tensor(st.seq_lens, device="cuda")
+        if "sparse" in which:
+            md = torch.from_numpy(np.ascontiguousarray(st.mask)).cuda()
+            tm = T.TileMask(md, st.mask.shape[0], st.mask.shape[1])
+            out = torch.empty_like(q)
+            flops = A.prefill_flops(spec.Hq, spec.D, st.seq_lens, st.mask)
+            med, p10, p90 = _median_ms(torch, lambda: T.attn_prefill(k, v, q, lens, mask=tm,
+                                                                     out=out), 5)
+            tf = flops / (med * 1e-3) / 1e12
+            print(json.dumps({"extra": "sparse", "workload": spec.name, "ms": round(med, 3),
+                              "p10_ms": round(p10, 3), "p90_ms": round(p90, 3),
+                              "flops": int(flops), "TFLOP/s": round(tf, 1),
+                              "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}), flush=True)
+            del out
+        if "maskgen" in which:
+            spm = 250
+            tm = T.tile_mask_generate(k, q, lens, spm)
+            ws = torch.empty(T.tile_mask_workspace_bytes(k, spec.context), dtype=torch.uint8,
+                             device="cuda")
+            med, p10, p90 = _median_ms(
+                torch, lambda: T.tile_mask_generate(k, q, lens, spm, out=tm.data, workspace=ws),
+                20)
+            nbytes = A.maskgen_bytes(spec.B, spec.Hq, spec.Hkv, spec.D, spec.context,
+                                     st.head_bits)
+            gbs = nbytes / (med * 1e-3) / 1e9
+            print(json.dumps({"extra": "maskgen", "workload": spec.name,
+                              "skip_per_mille": spm, "ms": round(med, 4),
+                              "p10_ms": round(p10, 4), "p90_ms": round(p90, 4),
+                              "bytes": int(nbytes), "GB/s": round(gbs, 1),
+                              "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                              "kept_tiles": int(tm.data.sum())}), flush=True)
+            del ws, tm
+        del k, v, q
+        torch.cuda.empty_cache()
+    if "chunk" in which:
+        B, Hq, Hkv, Lq, hist = 1, 32, 8, 512, 8192
+        cap = hist + Lq
+        kv = W.make_inputs(W.small("prefill", B=B, Hq=Hq, Hkv=Hkv, L=cap, bits=8, seed=901))
+        qn = W.make_inputs(W.small("prefill", B=B, Hq=Hq, Hkv=Hkv, L=Lq, bits=8, seed=902)).q
+        k = T.KVCache(B, Hkv, 128, cap, kv.structure.head_bits, T.LAYOUT_TOKEN)
+        v = T.KVCache(B, Hkv, 128, cap, kv.structure.head_bits, T.LAYOUT_CHANNEL)
+        T.kv_quantize(k, torch.from_numpy(kv.k).cuda(), 0)
+        T.kv_quantize(v, torch.from_numpy(kv.v).cuda(), 0)
+        q = torch.from_numpy(qn).cuda()
+        out = torch.empty_like(q)
+        lens = torch.tensor([cap], dtype=torch.int32, device="cuda")
+        starts = torch.tensor([hist], dtype=torch.int32, device="cuda")
+        xk = torch.from_numpy(np.ascontiguousarray(kv.k[:, :, hist:])).cuda()
+        xv = torch.from_numpy(np.ascontiguousarray(kv.v[:, :, hist:])).cuda()
+        flops = 4 * 128 * Hq * sum(hist + i + 1 for i in range(Lq))
+        med, _, _ = _median_ms(torch, lambda: T.attn_prefill_chunk(k, v, q, lens, cap, out=out),
+                               20)
+
+        def with_append():
+            T.kv_append(k, xk, starts)
+            T.kv_append(v, xv, starts)
+            T.attn_prefill_chunk(k, v, q, lens, cap, out=out)
+        med2, _, _ = _median_ms(torch, with_append, 20)
+        tf = flops / (med * 1e-3) / 1e12
+        print(json.dumps({"extra": "chunk", "workload": f"chunk {Lq} rows after {hist} cached",
+                          "ms": round(med, 4), "ms_with_append": round(med2, 4),
+                          "flops": int(flops), "TFLOP/s": round(tf, 1),
+                          "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}), flush=True)
+
+
 def cpu_baseline(inp, A, W):
     """The oracle as it stands on the prefill workload (all 32 query heads, all
     rows), process pool over heads."""
@@ -198,7 +297,10 @@ def main():
                     help="untimed steps first (the GPU clock takes about a second to settle)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "sparse", "maskgen", "chunk",
+                                       "extras"], default=None,
+                    help="one leg alone; sparse / maskgen / chunk (or all three: extras) "
+                         "print their own JSON lines")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy (for HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -223,6 +325,11 @@ def main():
         print(json.dumps({"copy_bytes": src.numel()}), flush=True)
         return
     T.device_check(0)
+
+    if args.only in ("sparse", "maskgen", "chunk", "extras"):
+        which = ["sparse", "maskgen", "chunk"] if args.only == "extras" else [args.only]
+        bench_extras(which, torch, T, W, A)
+        return
 
     if args.only == "decode":
         d = bench_decode(args, torch, T, W, A)

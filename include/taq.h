@@ -204,6 +204,43 @@ taq_status taq_attn_prefill_chunk(const taq_kv_cache* k_cache,
                                   const taq_tile_mask* mask, float softmax_scale,
                                   void* o_f16, void* stream);
 
+/* Workspace bytes that taq_tile_mask_generate needs (0 for an invalid
+ * descriptor or max_seq_len). */
+size_t taq_tile_mask_workspace_bytes(const taq_kv_cache* k_cache,
+                                     int32_t max_seq_len);
+
+/* Training-free KV-tile mask for block-sparse prefill, after the policy of
+ * section 2.3 of the block-sparse page: a coarse pattern of skipped 128x128
+ * blocks with dense local blocks and a capped skipped share.  That page
+ * predicts the pattern with a learned head; this call scores tiles from the
+ * data instead.  For batch entry b (n = seq_lens[b], nt_b = ceil(n / 128)),
+ * KV head g and query tile i < nt_b it keeps KV tile 0 and tile i and, of
+ * tiles 1 .. i-1, drops the floor((i-1) * skip_per_mille / 1000) with the
+ * lowest importance (ties: lower j first), where importance(i, j) =
+ * sum_d Qsum_i[d] * Kmean_j[d]: Qsum_i sums the query rows of tile i (rows
+ * < n) over the Hq/Hkv query heads of g, Kmean_j is the mean dequantised key
+ * of tile j.  The sums are exact, Kmean = double(Ksum) / count / 2^24 with
+ * the sums in units of 2^-24, and the dot product runs over d in order as
+ * double multiply then double add, so the result is reproducible bit for bit.
+ * Tiles above the diagonal and rows i >= nt_b are 0.
+ * q: fp16 [B][Hq][max_seq_len][128]; k_cache: TAQ_LAYOUT_TOKEN, head_dim 128;
+ * seq_lens: device int32 [B] (clamped to [0, max_seq_len]); mask_out: device
+ * uint8 [B][Hkv][nt][nt], nt = ceil(max_seq_len / 128), every byte written,
+ * usable as a taq_tile_mask with n_q_tiles = n_k_tiles = nt, stride_h = nt^2,
+ * stride_b = Hkv * nt^2; workspace: device, 16-byte aligned, of
+ * taq_tile_mask_workspace_bytes() bytes = B * Hkv * nt * (2 * 128 + nt) * 8,
+ * caller-owned (on return it holds the pooled sums and the scores).  max_seq_len is limited to 2048 tiles.  Errors:
+ * INVALID_ARGUMENT (null pointer, Hq not a multiple of Hkv, max_seq_len or
+ * skip_per_mille out of range), UNSUPPORTED (cache format, Hq / Hkv above
+ * 64, max_seq_len beyond 2048 tiles), MISALIGNED, WORKSPACE_TOO_SMALL.
+ * Non-finite queries or keys give an unspecified mask (tile 0 and the
+ * diagonal still kept). */
+taq_status taq_tile_mask_generate(const taq_kv_cache* k_cache, const void* q_f16,
+                                  int32_t num_q_heads, const int32_t* seq_lens,
+                                  int32_t max_seq_len, int32_t skip_per_mille,
+                                  uint8_t* mask_out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Test hook: when `arch` is non-NULL, taq_device_check compares this string
  * instead of the device's architecture name (NULL restores the real check). */
 void taq_debug_set_arch_override(const char* arch);

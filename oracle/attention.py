@@ -40,10 +40,15 @@ import numpy as np
 TILE = 128
 
 
-def _mask_for(mask, b):
+def _mask_for(mask, b, g):
+    """The [nq][nk] tile mask of batch entry b and KV head g; a mask given as
+    [nq][nk] is shared, [B][nq][nk] is per batch entry, [B][Hkv][nq][nk] per
+    batch entry and KV head."""
     if mask is None:
         return None
     m = np.asarray(mask)
+    if m.ndim == 4:
+        return m[b, g]
     return m[b] if m.ndim == 3 else m
 
 
@@ -101,7 +106,7 @@ def _job(args):
         q_rows = g["q"][b, h][None, :].astype(np.float64)
     pos = np.asarray(rows) + int(g.get("qoff", np.zeros(b + 1, dtype=np.int64))[b])
     return _rows_one_head(q_rows, pos, g["k"][b, kvh], g["v"][b, kvh],
-                          int(g["lens"][b]), _mask_for(g["mask"], b), g["tau"],
+                          int(g["lens"][b]), _mask_for(g["mask"], b, kvh), g["tau"],
                           g["causal"])
 
 
@@ -121,7 +126,8 @@ def prefill(q, k_hat, v_hat, seq_lens, mask=None, scale=None, rows=None,
     """Causal prefill attention.
 
     q: fp16 [B][Hq][L][D]; k_hat, v_hat: dequantised fp64 [B][Hkv][cap][D];
-    seq_lens: [B]; mask: None, [nq][nk] or [B][nq][nk] tile keep-mask.
+    seq_lens: [B]; mask: None, [nq][nk], [B][nq][nk] or [B][Hkv][nq][nk]
+    tile keep-mask (the last form one per KV head).
     rows: None (all L rows) or a 1-D array of query rows to evaluate.
     heads: None (all) or a list of (b, h) pairs.
     Returns fp64 [B][Hq][R][D] (R = L or len(rows)); heads not evaluated are 0.
@@ -147,8 +153,9 @@ def prefill_chunk(q, k_hat, v_hat, seq_lens, mask=None, scale=None, rows=None,
     """Chunked prefill: q fp16 [B][Hq][Lq][D] holds the last Lq positions of
     each sequence, whose keys and values are already in the cache, so row i of
     batch b sits at position seq_lens[b] - Lq + i (bottom-right alignment);
-    rows at negative positions are padding (zero).  mask: None, [nq][nk] or
-    [B][nq][nk] over positions.  Returns fp64 [B][Hq][R][D]."""
+    rows at negative positions are padding (zero).  mask: None, [nq][nk],
+    [B][nq][nk] or [B][Hkv][nq][nk] over positions.  Returns fp64
+    [B][Hq][R][D]."""
     B, Hq, Lq, D = q.shape
     Hkv = k_hat.shape[1]
     if Hq % Hkv:

@@ -193,3 +193,47 @@ def test_kv_append_rejects():
     assert L.taq_kv_append(ctypes.byref(cache(bits=(3, 4))), FAKE, FAKE, 4, None) == UNSUPPORTED
     if not os.path.exists("/dev/kfd"):
         assert L.taq_kv_append(ctypes.byref(d), FAKE, FAKE, 256, None) == HIP
+
+
+def maskgen_call(k=None, hq=8, max_len=1000, spm=250, q=FAKE, lens=FAKE, out=FAKE, ws=FAKE,
+                 ws_bytes=1 << 30):
+    k = k or cache(B=2, H=2, cap=1024, bits=(8, 4), layout=0)
+    return status_of(T.lib().taq_tile_mask_generate(ctypes.byref(k), q, hq, lens, max_len, spm,
+                                                    out, ws, ws_bytes, None))
+
+
+def test_tile_mask_workspace_bytes():
+    L = T.lib()
+    k = cache(B=2, H=2, cap=1024, bits=(8, 4), layout=0)
+    # query sums and key means (B * Hkv * nt * D doubles each) and scores
+    # (B * Hkv * nt * nt doubles), nt = ceil(1000 / 128) = 8
+    assert L.taq_tile_mask_workspace_bytes(ctypes.byref(k), 1000) == 2 * 2 * 8 * (256 + 8) * 8
+    assert L.taq_tile_mask_workspace_bytes(ctypes.byref(k), 0) == 0
+    assert L.taq_tile_mask_workspace_bytes(ctypes.byref(k), 2000) == 0        # beyond capacity
+    kd = cache(B=2, H=2, cap=1024, bits=(8, 4), layout=1)
+    assert L.taq_tile_mask_workspace_bytes(ctypes.byref(kd), 1000) == 0       # channel layout
+
+
+def test_tile_mask_rejects():
+    assert maskgen_call(hq=7)[0] == INVALID
+    assert maskgen_call(hq=0)[0] == INVALID
+    assert maskgen_call(max_len=1025)[0] == INVALID
+    assert maskgen_call(max_len=-1)[0] == INVALID
+    assert maskgen_call(spm=-1)[0] == INVALID
+    assert maskgen_call(spm=1001)[0] == INVALID
+    assert maskgen_call(q=0)[0] == INVALID
+    assert maskgen_call(lens=0)[0] == INVALID
+    assert maskgen_call(out=0)[0] == INVALID
+    assert maskgen_call(q=FAKE + 2)[0] == MISALIGNED
+    assert maskgen_call(lens=FAKE + 4)[0] == MISALIGNED
+    assert maskgen_call(ws=0)[0] == WS_SMALL
+    assert maskgen_call(ws_bytes=2 * 2 * 8 * (256 + 8) * 8 - 1)[0] == WS_SMALL
+    assert maskgen_call(ws=FAKE + 8)[0] == MISALIGNED
+    assert maskgen_call(k=cache(B=2, H=2, cap=1024, bits=(8, 4), layout=1))[0] == UNSUPPORTED
+    assert maskgen_call(k=cache(B=2, H=2, D=64, cap=1024, bits=(8, 4)))[0] == UNSUPPORTED
+    # at most 2048 tiles per side (262144 positions)
+    big = cache(B=1, H=1, cap=262272, bits=(8,))
+    assert maskgen_call(k=big, hq=1, max_len=262272)[0] == UNSUPPORTED
+    if not os.path.exists("/dev/kfd"):
+        assert maskgen_call(k=big, hq=1, max_len=262144)[0] == HIP   # valid: device query
+        assert maskgen_call(max_len=0)[0] == HIP

@@ -221,3 +221,32 @@ def test_chunk_of_one_row_is_decode():
     dec = att.decode(q, k, v, lens)
     chk = att.prefill_chunk(q[:, :, None, :], k, v, lens)
     np.testing.assert_allclose(chk[:, :, 0], dec, rtol=0, atol=1e-13)
+
+
+def test_per_kv_head_mask_selects_the_group_mask():
+    # a [B][Hkv][nq][nk] mask gives query head h of batch b the mask of KV head
+    # h // (Hq / Hkv): each (b, h) equals the run with that one [nq][nk] mask
+    # (the shared-mask path is pinned by brute force above)
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, L, D = 2, 4, 2, 300, 16
+    q = _rand(rng, (B, Hq, L, D))
+    k = _rand(rng, (B, Hkv, L, D)).astype(np.float64)
+    v = _rand(rng, (B, Hkv, L, D)).astype(np.float64)
+    lens = np.array([300, 260])
+    m = np.tile(np.tril(np.ones((3, 3), np.uint8)), (B, Hkv, 1, 1))
+    m[0, 1, 2, 1] = 0
+    m[1, 0, 1, 0] = 0
+    m[1, 1, 2, 0] = 0
+    m[1, 1, 2, 1] = 0
+    ours = att.prefill(q, k, v, lens, mask=m)
+    for b in range(B):
+        for h in range(Hq):
+            one = att.prefill(q, k, v, lens, mask=m[b, h // 2], heads=[(b, h)])
+            np.testing.assert_array_equal(ours[b, h], one[b, h])
+    # the four masks differ, so a swapped index would change some head
+    assert len({m[b, g].tobytes() for b in range(B) for g in range(Hkv)}) == 4
+    chunk = att.prefill_chunk(q[:, :, 200:], k, v, lens, mask=m)
+    for b in range(B):
+        for h in range(Hq):
+            one = att.prefill_chunk(q[:, :, 200:], k, v, lens, mask=m[b, h // 2], heads=[(b, h)])
+            np.testing.assert_array_equal(chunk[b, h], one[b, h])

@@ -31,7 +31,8 @@ EXPORTS = ("taq_last_error", "taq_abi_version", "taq_device_check",
            "taq_kv_codes_bytes", "taq_kv_meta_count", "taq_kv_quantize",
            "taq_kv_dequantize", "taq_attn_decode_workspace_bytes",
            "taq_attn_decode", "taq_attn_prefill", "taq_debug_set_arch_override",
-           "taq_kv_append", "taq_attn_prefill_chunk")
+           "taq_kv_append", "taq_attn_prefill_chunk", "taq_tile_mask_workspace_bytes",
+           "taq_tile_mask_generate")
 
 
 class TaqError(RuntimeError):
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
         "taq_debug_set_arch_override": (None, [ctypes.c_char_p]),
         "taq_kv_append": (ctypes.c_int, [CP, P, P, I32, P]),
         "taq_attn_prefill_chunk": (ctypes.c_int, [CP, CP, P, I32, I32, P, I32, MP, F, P, P]),
+        "taq_tile_mask_workspace_bytes": (SZ, [CP, I32]),
+        "taq_tile_mask_generate": (ctypes.c_int, [CP, P, I32, P, I32, I32, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -265,3 +268,33 @@ def attn_prefill_chunk(k: KVCache, v: KVCache, q, seq_lens, max_seq_len: int,
                                         ctypes.byref(md) if md is not None else None,
                                         softmax_scale, _ptr(out), _stream(q.device)))
     return out
+
+
+def tile_mask_workspace_bytes(k: KVCache, max_seq_len: int) -> int:
+    d = k.desc()
+    return int(lib().taq_tile_mask_workspace_bytes(ctypes.byref(d), max_seq_len))
+
+
+def tile_mask_generate(k: KVCache, q, seq_lens, skip_per_mille: int, out=None, workspace=None):
+    """Training-free KV-tile mask from the queries and the quantised keys:
+    returns a TileMask over a uint8 [B][Hkv][nt][nt] tensor (nt =
+    ceil(L / 128) for q fp16 [B][Hq][L][D])."""
+    import torch
+    B, Hq, L, D = q.shape
+    nt = (L + 127) // 128
+    if q.dtype != torch.float16 or not q.is_contiguous() or q.dim() != 4:
+        raise ValueError("q must be a contiguous fp16 [B][Hq][L][D] tensor")
+    if out is None:
+        out = torch.empty((B, k.num_kv_heads, nt, nt), dtype=torch.uint8, device=q.device)
+    elif (out.dtype != torch.uint8 or not out.is_contiguous()
+          or tuple(out.shape) != (B, k.num_kv_heads, nt, nt)):
+        raise ValueError("out must be a contiguous uint8 [B][Hkv][nt][nt] tensor")
+    if workspace is None:
+        nb = tile_mask_workspace_bytes(k, L)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)
+    kd = k.desc()
+    _check(lib().taq_tile_mask_generate(ctypes.byref(kd), _ptr(q), Hq, _ptr(seq_lens), L,
+                                        int(skip_per_mille), _ptr(out), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(q.device)))
+    return TileMask(out, nt, nt, stride_b=k.num_kv_heads * nt * nt, stride_h=nt * nt)

@@ -372,4 +372,67 @@ taq_status taq_kv_append(const taq_kv_cache* c, const void* x, const int32_t* st
   return e == hipSuccess ? TAQ_OK : hip_fail(e, "kv_append launch");
 }
 
+size_t taq_tile_mask_workspace_bytes(const taq_kv_cache* k, int32_t max_len) {
+  if (check_cache(k, "k_cache", TAQ_LAYOUT_TOKEN, true) != TAQ_OK) return 0;
+  if (max_len < 0 || max_len > k->capacity) return 0;
+  const size_t nt = (size_t)(max_len + TAQ_TILE - 1) / TAQ_TILE;
+  // query sums and key means [B][Hkv][nt][D] each, scores [B][Hkv][nt][nt]
+  return (size_t)k->batch * k->num_kv_heads * nt * (2 * k->head_dim + nt) * sizeof(double);
+}
+
+taq_status taq_tile_mask_generate(const taq_kv_cache* k, const void* q, int32_t hq,
+                                  const int32_t* lens, int32_t max_len,
+                                  int32_t skip_per_mille, uint8_t* mask_out, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  taq_status st = check_cache(k, "k_cache", TAQ_LAYOUT_TOKEN, true);
+  if (st) return st;
+  if (hq < 1 || hq % k->num_kv_heads)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "num_q_heads (%d) must be a positive multiple of "
+                "num_kv_heads (%d)", hq, k->num_kv_heads);
+  if (hq / k->num_kv_heads > 64)
+    return fail(TAQ_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads = %d (at most 64)",
+                hq / k->num_kv_heads);
+  if (max_len < 0 || max_len > k->capacity)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "max_seq_len %d outside [0, capacity %d]", max_len,
+                k->capacity);
+  {
+    const int64_t nt = (max_len + TAQ_TILE - 1) / TAQ_TILE, nb = (nt + 63) / 64;
+    const int64_t bh = (int64_t)k->batch * k->num_kv_heads;
+    if (bh * nt > INT32_MAX || bh * nb * nb > INT32_MAX)
+      return fail(TAQ_ERR_UNSUPPORTED, "batch * num_kv_heads * tiles beyond the grid limit");
+  }
+  if (max_len > taq::MASKGEN_MAX_TILES * TAQ_TILE)
+    return fail(TAQ_ERR_UNSUPPORTED, "max_seq_len %d beyond %d tiles", max_len,
+                taq::MASKGEN_MAX_TILES);
+  if (skip_per_mille < 0 || skip_per_mille > 1000)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "skip_per_mille %d outside [0, 1000]", skip_per_mille);
+  if (!q || !lens || !mask_out) return fail(TAQ_ERR_INVALID_ARGUMENT, "null q, seq_lens or mask");
+  if (!aligned16(q) || !aligned16(lens))
+    return fail(TAQ_ERR_MISALIGNED, "q and seq_lens must be 16-byte aligned");
+  const size_t need = taq_tile_mask_workspace_bytes(k, max_len);
+  if (!ws || ws_bytes < need)
+    return fail(TAQ_ERR_WORKSPACE_TOO_SMALL, "workspace: need %zu bytes, got %zu", need,
+                ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(TAQ_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  st = device_ok();
+  if (st) return st;
+  if (max_len == 0) return TAQ_OK;
+  taq::MaskGenArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.k = geom_of(k);
+  a.q = static_cast<const uint16_t*>(q);
+  a.lens = lens;
+  a.mask = mask_out;
+  a.nt = (max_len + TAQ_TILE - 1) / TAQ_TILE;
+  a.qsum = static_cast<double*>(ws);
+  a.kmean = a.qsum + (size_t)k->batch * k->num_kv_heads * a.nt * k->head_dim;
+  a.score = a.kmean + (size_t)k->batch * k->num_kv_heads * a.nt * k->head_dim;
+  a.Hq = hq;
+  a.r = hq / k->num_kv_heads;
+  a.L = max_len;
+  a.skip_per_mille = skip_per_mille;
+  hipError_t e = taq::launch_tile_mask(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TAQ_OK : hip_fail(e, "tile_mask launch");
+}
+
 }  // extern "C"

@@ -60,6 +60,20 @@ struct PrefillArgs {
   uint8_t heads[TAQ_MAX_KV_HEADS];
 };
 
+// Training-free KV-tile mask generator (per (batch, KV head) 128x128 masks).
+constexpr int MASKGEN_MAX_TILES = 2048;   // tiles per side (max_seq_len <= 262144)
+struct MaskGenArgs {
+  CacheGeom k;
+  const uint16_t* q;     // [B][Hq][L][D]
+  const int32_t* lens;
+  uint8_t* mask;         // [B][Hkv][nt][nt]
+  double* qsum;          // workspace [B][Hkv][nt][D]: query sums in units of 2^-24
+  double* kmean;         // workspace [B][Hkv][D][nt]: mean dequantised key per tile
+  double* score;         // workspace [B][Hkv][nt][nt]: importance (lower triangle)
+  int32_t Hq, r, L, nt, skip_per_mille;
+};
+hipError_t launch_tile_mask(const MaskGenArgs& a, hipStream_t s);
+
 hipError_t launch_kv_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_kv_dequantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t s);

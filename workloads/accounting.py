@@ -76,6 +76,15 @@ def prefill_flops(Hq: int, D: int, seq_lens, mask=None) -> int:
     return 4 * D * Hq * total
 
 
+def maskgen_bytes(B: int, Hq: int, Hkv: int, D: int, L: int, head_bits) -> int:
+    """Algorithmic bytes of the tile-mask generator over full-length sequences:
+    fp16 Q read once, the K cache (codes, scales, zeros) read once, and the
+    uint8 [B][Hkv][nt][nt] mask written once."""
+    nt = -(-L // TILE)
+    k_bytes = sum(token_bytes(D, int(b)) for b in head_bits) * L
+    return B * (Hq * L * D * 2 + k_bytes + Hkv * nt * nt)
+
+
 def score_matrix_bytes(n: int, elem_bytes: int = 2) -> int:
     """Bytes of a full n x n score matrix (what tiling never materialises)."""
     return n * n * elem_bytes
