@@ -191,7 +191,9 @@ def bench_extras(which, torch, T, W, A):
     sparse   attn_prefill on the 128K workload with its seeded 25% tile mask;
     maskgen  tile_mask_generate (skip 250 per mille) on the same Q and K;
     chunk    a 512-row chunk against 8192 cached tokens (Hq 32, Hkv 8, int8),
-             alone and with the two kv_append calls of the new tokens."""
+             alone and with the two kv_append calls of the new tokens;
+    twopass  the long-context decode with the online softmax and with the
+             literal two-pass softmax (same algorithmic bytes; pass 1 re-reads K)."""
     if {"sparse", "maskgen"} & set(which):
         spec = W.WORKLOADS["prefill_128k_sparse"]
         log(f"generating {spec.name}")
@@ -234,6 +236,30 @@ def bench_extras(which, torch, T, W, A):
                               "kept_tiles": int(tm.data.sum())}), flush=True)
             del ws, tm
         del k, v, q
+        torch.cuda.empty_cache()
+    if "twopass" in which:
+        spec = W.WORKLOADS["decode_128k_mixed"]
+        log(f"generating {spec.name}")
+        inp = W.make_inputs(spec)
+        k, v = make_caches(T, inp, torch)
+        T.kv_quantize(k, torch.from_numpy(inp.k).cuda(), 0)
+        T.kv_quantize(v, torch.from_numpy(inp.v).cuda(), 0)
+        q = torch.from_numpy(inp.q).cuda()
+        out = torch.empty_like(q)
+        lens = torch.tensor(inp.structure.seq_lens, device="cuda")
+        ws = torch.empty(T.decode_workspace_bytes(k, spec.Hq, spec.max_len), dtype=torch.uint8,
+                         device="cuda")
+        nbytes = A.decode_bytes(spec.B, spec.Hq, spec.D, inp.structure.seq_lens,
+                                inp.structure.head_bits)
+        res = {}
+        for name, tp in (("online", False), ("two_pass", True)):
+            med, p10, p90 = _median_ms(torch, lambda: T.attn_decode(
+                k, v, q, lens, spec.max_len, out=out, workspace=ws, two_pass=tp), 50)
+            res[name] = {"us": round(med * 1e3, 1), "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1)}
+        print(json.dumps({"extra": "twopass", "workload": spec.name, "bytes": int(nbytes), **res,
+                          "two_pass_over_online": round(res["two_pass"]["us"] /
+                                                        res["online"]["us"], 3)}), flush=True)
+        del k, v, q, out, ws
         torch.cuda.empty_cache()
     if "chunk" in which:
         B, Hq, Hkv, Lq, hist = 1, 32, 8, 512, 8192
@@ -298,9 +324,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--only", choices=["prefill", "decode", "sparse", "maskgen", "chunk",
-                                       "extras"], default=None,
-                    help="one leg alone; sparse / maskgen / chunk (or all three: extras) "
-                         "print their own JSON lines")
+                                       "twopass", "extras"], default=None,
+                    help="one leg alone; sparse / maskgen / chunk / twopass (or all four: "
+                         "extras) print their own JSON lines")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy (for HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -326,8 +352,9 @@ def main():
         return
     T.device_check(0)
 
-    if args.only in ("sparse", "maskgen", "chunk", "extras"):
-        which = ["sparse", "maskgen", "chunk"] if args.only == "extras" else [args.only]
+    if args.only in ("sparse", "maskgen", "chunk", "twopass", "extras"):
+        which = (["sparse", "maskgen", "chunk", "twopass"] if args.only == "extras"
+                 else [args.only])
         bench_extras(which, torch, T, W, A)
         return
 

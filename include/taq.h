@@ -176,6 +176,21 @@ taq_status taq_attn_decode(const taq_kv_cache* k_cache,
                            float softmax_scale, void* o_f16, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* The same decode attention with the literal two-pass softmax: pass 1 reads
+ * K only and finds each query head's exact maximum score, pass 2 accumulates
+ * exp(s - max) v and exp(s - max) against that fixed maximum with no
+ * rescaling, and the chunk partials are added.  This is the plain reading of
+ * the "coarse maximum first, then correct the normaliser" wording of section
+ * 2.2 of the block-sparse page, kept as an ablation and cross-check of the
+ * online merge that taq_attn_decode uses (it reads K twice).  Arguments,
+ * workspace size and errors as taq_attn_decode. */
+taq_status taq_attn_decode_two_pass(const taq_kv_cache* k_cache,
+                                    const taq_kv_cache* v_cache, const void* q_f16,
+                                    int32_t num_q_heads, const int32_t* seq_lens,
+                                    int32_t max_seq_len, const taq_tile_mask* mask,
+                                    float softmax_scale, void* o_f16, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* Causal prefill with equal query and key lengths: q/o [B][Hq][L][D] where
  * L = max_seq_len; row i of batch b attends to keys j <= i, j < seq_lens[b],
  * in tiles the mask keeps (NULL = dense causal).  Query-row tiles whose whole

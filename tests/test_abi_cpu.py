@@ -92,6 +92,16 @@ def decode_call(k=None, v=None, hq=8, max_len=200, mask=None, ws_bytes=1 << 30,
                                              max_len, m, scale, o, ws, ws_bytes, None))
 
 
+def decode_two_pass_call(k=None, v=None, hq=8, max_len=200, mask=None, ws_bytes=1 << 30,
+                         q=FAKE, o=FAKE, lens=FAKE, ws=FAKE, scale=0.0):
+    k = k or cache(B=1, H=2, cap=256, bits=(8, 8), layout=0)
+    v = v or cache(B=1, H=2, cap=256, bits=(8, 8), layout=1)
+    m = ctypes.byref(mask) if mask is not None else None
+    return status_of(T.lib().taq_attn_decode_two_pass(ctypes.byref(k), ctypes.byref(v), q, hq,
+                                                      lens, max_len, m, scale, o, ws, ws_bytes,
+                                                      None))
+
+
 def prefill_call(k=None, v=None, hq=8, max_len=200, mask=None, q=FAKE, o=FAKE, lens=FAKE,
                  scale=0.0):
     k = k or cache(B=1, H=2, cap=256, bits=(8, 8), layout=0)
@@ -101,7 +111,7 @@ def prefill_call(k=None, v=None, hq=8, max_len=200, mask=None, q=FAKE, o=FAKE, l
                                               max_len, m, scale, o, None))
 
 
-@pytest.mark.parametrize("call", [decode_call, prefill_call])
+@pytest.mark.parametrize("call", [decode_call, decode_two_pass_call, prefill_call])
 def test_attention_rejects(call):
     assert call(hq=7)[0] == INVALID                      # Hq % Hkv != 0
     assert call(hq=6)[0] == UNSUPPORTED                  # r = 3
@@ -131,6 +141,7 @@ def test_attention_rejects(call):
 def test_decode_workspace_too_small():
     assert decode_call(ws_bytes=16)[0] == WS_SMALL
     assert decode_call(ws=0)[0] == WS_SMALL
+    assert decode_two_pass_call(ws_bytes=16)[0] == WS_SMALL
 
 
 def test_valid_arguments_reach_the_device_check():
@@ -139,6 +150,8 @@ def test_valid_arguments_reach_the_device_check():
     if os.path.exists("/dev/kfd"):
         pytest.skip("a GPU device node is present")
     rc, msg = decode_call()
+    assert rc == HIP, msg
+    rc, msg = decode_two_pass_call()
     assert rc == HIP, msg
     rc, msg = prefill_call()
     assert rc == HIP, msg

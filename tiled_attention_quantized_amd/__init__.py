@@ -32,7 +32,7 @@ EXPORTS = ("taq_last_error", "taq_abi_version", "taq_device_check",
            "taq_kv_dequantize", "taq_attn_decode_workspace_bytes",
            "taq_attn_decode", "taq_attn_prefill", "taq_debug_set_arch_override",
            "taq_kv_append", "taq_attn_prefill_chunk", "taq_tile_mask_workspace_bytes",
-           "taq_tile_mask_generate")
+           "taq_tile_mask_generate", "taq_attn_decode_two_pass")
 
 
 class TaqError(RuntimeError):
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
         "taq_kv_dequantize": (ctypes.c_int, [CP, I32, I32, P, P, P]),
         "taq_attn_decode_workspace_bytes": (SZ, [CP, I32, I32]),
         "taq_attn_decode": (ctypes.c_int, [CP, CP, P, I32, P, I32, MP, F, P, P, SZ, P]),
+        "taq_attn_decode_two_pass": (ctypes.c_int, [CP, CP, P, I32, P, I32, MP, F, P, P, SZ, P]),
         "taq_attn_prefill": (ctypes.c_int, [CP, CP, P, I32, P, I32, MP, F, P, P]),
         "taq_debug_set_arch_override": (None, [ctypes.c_char_p]),
         "taq_kv_append": (ctypes.c_int, [CP, P, P, I32, P]),
@@ -215,8 +216,9 @@ def decode_workspace_bytes(k: KVCache, num_q_heads: int, max_seq_len: int) -> in
 
 def attn_decode(k: KVCache, v: KVCache, q, seq_lens, max_seq_len: int,
                 mask: Optional[TileMask] = None, softmax_scale: float = 0.0,
-                out=None, workspace=None):
-    """Decode attention; q fp16 [B][Hq][D], seq_lens int32 [B] on the device."""
+                out=None, workspace=None, two_pass: bool = False):
+    """Decode attention; q fp16 [B][Hq][D], seq_lens int32 [B] on the device.
+    two_pass=True runs the literal two-pass softmax (global maximum first)."""
     import torch
     B, Hq, D = q.shape
     if out is None:
@@ -226,12 +228,11 @@ def attn_decode(k: KVCache, v: KVCache, q, seq_lens, max_seq_len: int,
         workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
     kd, vd = k.desc(), v.desc()
     md = mask.desc() if mask is not None else None
-    _check(lib().taq_attn_decode(ctypes.byref(kd), ctypes.byref(vd), _ptr(q), Hq,
-                                 _ptr(seq_lens), max_seq_len,
-                                 ctypes.byref(md) if md is not None else None,
-                                 softmax_scale, _ptr(out), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(),
-                                 _stream(q.device)))
+    fn = lib().taq_attn_decode_two_pass if two_pass else lib().taq_attn_decode
+    _check(fn(ctypes.byref(kd), ctypes.byref(vd), _ptr(q), Hq, _ptr(seq_lens), max_seq_len,
+              ctypes.byref(md) if md is not None else None, softmax_scale, _ptr(out),
+              _ptr(workspace), workspace.numel() * workspace.element_size(),
+              _stream(q.device)))
     return out
 
 

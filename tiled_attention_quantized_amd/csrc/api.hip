@@ -230,10 +230,15 @@ size_t taq_attn_decode_workspace_bytes(const taq_kv_cache* k, int32_t hq, int32_
   return (size_t)k->batch * hq * nchunk * (128 + 2) * sizeof(float);
 }
 
-taq_status taq_attn_decode(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
-                           int32_t hq, const int32_t* lens, int32_t max_len,
-                           const taq_tile_mask* mask, float softmax_scale, void* o,
-                           void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of taq_attn_decode (online softmax) and taq_attn_decode_two_pass.
+taq_status decode_common(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
+                         int32_t hq, const int32_t* lens, int32_t max_len,
+                         const taq_tile_mask* mask, float softmax_scale, void* o, void* ws,
+                         size_t ws_bytes, void* stream, bool two_pass) {
   taq_status st = check_pair(k, v, hq, max_len);
   if (st) return st;
   if (!q || !o || !lens) return fail(TAQ_ERR_INVALID_ARGUMENT, "null q, o or seq_lens");
@@ -272,8 +277,29 @@ taq_status taq_attn_decode(const taq_kv_cache* k, const taq_kv_cache* v, const v
   a.chunk = taq::decode_chunk_tokens(k->batch, k->num_kv_heads, max_len);
   a.nchunk = max_len > 0 ? (max_len + a.chunk - 1) / a.chunk : 1;
   a.scale_log2 = scale_log2_of(softmax_scale, 128);
-  hipError_t e = taq::launch_attn_decode(a, static_cast<hipStream_t>(stream));
+  hipError_t e = taq::launch_attn_decode(a, static_cast<hipStream_t>(stream), two_pass);
   return e == hipSuccess ? TAQ_OK : hip_fail(e, "attn_decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+taq_status taq_attn_decode(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
+                           int32_t hq, const int32_t* lens, int32_t max_len,
+                           const taq_tile_mask* mask, float softmax_scale, void* o,
+                           void* ws, size_t ws_bytes, void* stream) {
+  return decode_common(k, v, q, hq, lens, max_len, mask, softmax_scale, o, ws, ws_bytes, stream,
+                       false);
+}
+
+taq_status taq_attn_decode_two_pass(const taq_kv_cache* k, const taq_kv_cache* v,
+                                    const void* q, int32_t hq, const int32_t* lens,
+                                    int32_t max_len, const taq_tile_mask* mask,
+                                    float softmax_scale, void* o, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  return decode_common(k, v, q, hq, lens, max_len, mask, softmax_scale, o, ws, ws_bytes, stream,
+                       true);
 }
 
 }  // extern "C"

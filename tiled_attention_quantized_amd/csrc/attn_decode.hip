@@ -18,6 +18,12 @@
 //    per query head.
 //  * a second kernel merges the chunk partials of each (batch, query head) in
 //    chunk order and writes fp16 O.
+//  * two-pass variant (the literal reading of the "coarse max first, then fix
+//    the normaliser" wording of section 2.2, kept as an ablation and cross-check
+//    of the online merge): pass 1 runs the same score path and writes each
+//    chunk's exact maximum; pass 2 takes the global maximum of its query head
+//    from those partials, accumulates exp2(s - M) v and exp2(s - M) with no
+//    rescaling, and the merge adds the chunk partials.  Pass 1 reads K only.
 //
 // Per step, both contractions run on the matrix cores (v_mfma_f32_16x16x32_f16):
 //  * scores: A = block-diagonal Q (row = (head, quant group), 16 rows per block
@@ -39,6 +45,11 @@ constexpr int D = 128;
 constexpr int STEP = 32;       // tokens per wave step
 constexpr int WAVES = 4;
 constexpr float NEG_BIG = -1.0e30f;
+
+// Softmax schedule of a decode launch.
+constexpr int ONLINE = 0;      // running max with lazy rescale, one pass
+constexpr int MAX_PASS = 1;    // two-pass, pass 1: exact maximum of the chunk
+constexpr int FIXED_MAX = 2;   // two-pass, pass 2: weights against the global maximum
 
 // Token of QK column t' (0..15) in QK block bk (0/1) of a step: chosen so that
 // lane t' holds the token pair that the PV operand packs as one dword.
@@ -135,7 +146,7 @@ struct WaveState {
   f32x4 acc[8];
 };
 
-template <int R, bool K8, bool V8>
+template <int R, bool K8, bool V8, int MODE>
 __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K8, V8>& ws,
                                              StepData& s, int nvalid, int i16, int lg) {
   constexpr int NRB = WaveState<R, K8, V8>::NRB;
@@ -191,28 +202,42 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
     }
   }
 
+  if constexpr (MODE == MAX_PASS) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+      ws.m_run[rb] = fmaxf(ws.m_run[rb], row16_max(fmaxf(sc[rb][0], sc[rb][1])));
+    return;
+  }
+
   // ---------------- online softmax ----------------
   // The running maximum m is only moved when the tile maximum exceeds it by
   // more than 2^8 (log2 units): weights exp2(s - m) then stay below 256, exact
   // enough in fp16, and the accumulator is rescaled only on those steps.  The
-  // final O = acc / l is unchanged by the choice of m.
+  // final O = acc / l is unchanged by the choice of m.  With FIXED_MAX, m is
+  // the global maximum from pass 1 and never moves (weights <= 1).
   uint32_t p2[NRB];
   float alpha[NRB];
   bool any_move = false;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const float mx = row16_max(fmaxf(sc[rb][0], sc[rb][1]));
-    const bool move = mx > ws.m_run[rb] + 8.f;
-    const float mn = move ? mx : ws.m_run[rb];
-    alpha[rb] = move ? fast_exp2(ws.m_run[rb] - mn) : 1.f;
+    bool move = false;
+    if constexpr (MODE == ONLINE) {
+      const float mx = row16_max(fmaxf(sc[rb][0], sc[rb][1]));
+      move = mx > ws.m_run[rb] + 8.f;
+      const float mn = move ? mx : ws.m_run[rb];
+      alpha[rb] = move ? fast_exp2(ws.m_run[rb] - mn) : 1.f;
+      ws.m_run[rb] = mn;
+    } else {
+      alpha[rb] = 1.f;
+    }
     any_move |= move;
-    ws.m_run[rb] = mn;
+    const float mn = ws.m_run[rb];
     const _Float16 p0 = (_Float16)fast_exp2(sc[rb][0] - mn);
     const _Float16 p1 = (_Float16)fast_exp2(sc[rb][1] - mn);
     ws.l_run[rb] = fmaf(ws.l_run[rb], alpha[rb], (float)p0 + (float)p1);
     p2[rb] = h2_to_u32(half2v{p0, p1});
   }
-  const bool rescale = __any(any_move);
+  const bool rescale = MODE == ONLINE && __any(any_move);
 
   // ---------------- gather P^T and alpha into the PV layout ----------------
   const int hcol = i16;
@@ -269,7 +294,7 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
   }
 }
 
-template <int R, bool K8, bool V8>
+template <int R, bool K8, bool V8, int MODE>
 __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, float* lds) {
   constexpr int NRB = (R + 3) / 4;
   const int lane = threadIdx.x & 63;
@@ -322,6 +347,22 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
   }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) { ws.m_run[rb] = NEG_BIG; ws.l_run[rb] = 0.f; }
+  if constexpr (MODE == FIXED_MAX) {
+    // global maximum of each query head: the largest of the pass-1 chunk maxima
+    const int nc = (n + a.chunk - 1) / a.chunk;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int h = 4 * rb + lg;
+      if (h < R) {
+        const float* src = a.ws + ((int64_t)b * a.Hq + g * R + h) * a.nchunk * (D + 2);
+        float M = NEG_BIG;
+        for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, src[(int64_t)cc * (D + 2)]);
+        ws.m_run[rb] = M;
+      } else {
+        ws.m_run[rb] = 0.f;   // rows past the r heads: score 0, weight 1, never used
+      }
+    }
+  }
 #pragma unroll
   for (int db = 0; db < 8; ++db) ws.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -357,12 +398,12 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
     int t_nxt = next_step(t_cur + STEP);
     load_step<K8, V8>(p, t_nxt < t_end ? t_nxt : t_safe, i16, lg, Bf);
     while (true) {
-      compute_step<R, K8, V8>(a, ws, A, t_end - t_cur, i16, lg);
+      compute_step<R, K8, V8, MODE>(a, ws, A, t_end - t_cur, i16, lg);
       t_cur = t_nxt;
       if (t_cur >= t_end) break;
       t_nxt = next_step(t_cur + STEP);
       load_step<K8, V8>(p, t_nxt < t_end ? t_nxt : t_safe, i16, lg, A);
-      compute_step<R, K8, V8>(a, ws, Bf, t_end - t_cur, i16, lg);
+      compute_step<R, K8, V8, MODE>(a, ws, Bf, t_end - t_cur, i16, lg);
       t_cur = t_nxt;
       if (t_cur >= t_end) break;
       t_nxt = next_step(t_cur + STEP);
@@ -375,6 +416,22 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
   float* sm = lds;
   float* sl = lds + WAVES * R;
   float* so = lds + 2 * WAVES * R;
+  if constexpr (MODE == MAX_PASS) {
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int h = 4 * rb + lg;
+      if (i16 == 0 && h < R) sm[w * R + h] = ws.m_run[rb];
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {
+      const int h = threadIdx.x;
+      float M = sm[h];
+#pragma unroll
+      for (int ww = 1; ww < WAVES; ++ww) M = fmaxf(M, sm[ww * R + h]);
+      a.ws[(((int64_t)b * a.Hq + g * R + h) * a.nchunk + c) * (D + 2)] = M;
+    }
+    return;
+  }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const float lt = row16_sum(ws.l_run[rb]);
@@ -401,14 +458,15 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
     float o = 0.f, l = 0.f;
 #pragma unroll
     for (int ww = 0; ww < WAVES; ++ww) {
-      const float f = fast_exp2(sm[ww * R + h] - M);
+      // FIXED_MAX: every wave used the same maximum, the weights add as they are
+      const float f = MODE == FIXED_MAX ? 1.f : fast_exp2(sm[ww * R + h] - M);
       o = fmaf(so[(ww * R + h) * D + d], f, o);
       l = fmaf(sl[ww * R + h], f, l);
     }
     float* dst = a.ws + (((int64_t)b * a.Hq + g * R + h) * nchunk + c) * (D + 2);
     dst[2 + d] = o;
     if (d == 0) {
-      dst[0] = M;
+      if (MODE == ONLINE) dst[0] = M;    // FIXED_MAX: slot 0 keeps the pass-1 maximum
       dst[1] = l;
     }
   }
@@ -417,7 +475,7 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
 #ifndef TAQ_DECODE_WAVES_INT4
 #define TAQ_DECODE_WAVES_INT4 3
 #endif
-template <int R, bool K8, bool V8>
+template <int R, bool K8, bool V8, int MODE>
 __global__ void __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu((K8 || V8) ? 2 : TAQ_DECODE_WAVES_INT4, (K8 || V8) ? 2 : TAQ_DECODE_WAVES_INT4)))
 decode_split_kernel(DecodeArgs a) {
@@ -435,11 +493,13 @@ decode_split_kernel(DecodeArgs a) {
   int n = a.lens[b];
   n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
   if (c * a.chunk >= n) return;
-  decode_body<R, K8, V8>(a, b, g, c, n, lds);
+  decode_body<R, K8, V8, MODE>(a, b, g, c, n, lds);
 }
 
 // One wave per (batch, query head): lanes own chunks for the max / normaliser
-// and channel pairs (2 * lane, 2 * lane + 1) for the accumulator.
+// and channel pairs (2 * lane, 2 * lane + 1) for the accumulator.  TWO_PASS:
+// every chunk's partials are relative to the same global maximum, so they add.
+template <bool TWO_PASS>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
@@ -459,7 +519,7 @@ decode_merge_kernel(DecodeArgs a) {
     const int c = c0 + lane;
     float f = 0.f;
     if (c < nc) {
-      f = fast_exp2(src[(int64_t)c * (D + 2)] - M);
+      f = TWO_PASS ? 1.f : fast_exp2(src[(int64_t)c * (D + 2)] - M);
       l = fmaf(src[(int64_t)c * (D + 2) + 1], f, l);
     }
     const int cn = min(64, nc - c0);
@@ -489,7 +549,7 @@ int decode_chunk_tokens(int B, int Hkv, int max_len) {
   return chunk;
 }
 
-template <int R>
+template <int R, int MODE>
 hipError_t launch_variants(DecodeArgs a, hipStream_t s) {
   // group the KV heads by their (K bits, V bits) variant
   for (int var = 0; var < 4; ++var) {
@@ -501,10 +561,10 @@ hipError_t launch_variants(DecodeArgs a, hipStream_t s) {
     if (a.nheads == 0) continue;
     const dim3 grid(a.nchunk * a.nheads * a.k.B);
     switch (var) {
-      case 0: hipLaunchKernelGGL((decode_split_kernel<R, false, false>), grid, dim3(256), 0, s, a); break;
-      case 1: hipLaunchKernelGGL((decode_split_kernel<R, false, true>), grid, dim3(256), 0, s, a); break;
-      case 2: hipLaunchKernelGGL((decode_split_kernel<R, true, false>), grid, dim3(256), 0, s, a); break;
-      default: hipLaunchKernelGGL((decode_split_kernel<R, true, true>), grid, dim3(256), 0, s, a); break;
+      case 0: hipLaunchKernelGGL((decode_split_kernel<R, false, false, MODE>), grid, dim3(256), 0, s, a); break;
+      case 1: hipLaunchKernelGGL((decode_split_kernel<R, false, true, MODE>), grid, dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((decode_split_kernel<R, true, false, MODE>), grid, dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL((decode_split_kernel<R, true, true, MODE>), grid, dim3(256), 0, s, a); break;
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -512,18 +572,31 @@ hipError_t launch_variants(DecodeArgs a, hipStream_t s) {
   return hipSuccess;
 }
 
-hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t s) {
-  hipError_t e;
+template <int MODE>
+hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
   switch (a.r) {
-    case 1: e = launch_variants<1>(a, s); break;
-    case 2: e = launch_variants<2>(a, s); break;
-    case 4: e = launch_variants<4>(a, s); break;
-    case 8: e = launch_variants<8>(a, s); break;
+    case 1: return launch_variants<1, MODE>(a, s);
+    case 2: return launch_variants<2, MODE>(a, s);
+    case 4: return launch_variants<4, MODE>(a, s);
+    case 8: return launch_variants<8, MODE>(a, s);
     default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t s, bool two_pass) {
+  hipError_t e;
+  if (two_pass) {
+    e = launch_split<MAX_PASS>(a, s);
+    if (e == hipSuccess) e = launch_split<FIXED_MAX>(a, s);
+  } else {
+    e = launch_split<ONLINE>(a, s);
   }
   if (e != hipSuccess) return e;
   const int nbh = a.k.B * a.Hq;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((nbh + 3) / 4), dim3(256), 0, s, a);
+  if (two_pass)
+    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((nbh + 3) / 4), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((nbh + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -76,7 +76,7 @@ hipError_t launch_tile_mask(const MaskGenArgs& a, hipStream_t s);
 
 hipError_t launch_kv_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_kv_dequantize(const QuantArgs& a, hipStream_t s);
-hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t s, bool two_pass);
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t s);
 
 // Decode split geometry chosen on the host (used for workspace sizing too).
