@@ -193,7 +193,9 @@ def bench_extras(which, torch, T, W, A):
     chunk    a 512-row chunk against 8192 cached tokens (Hq 32, Hkv 8, int8),
              alone and with the two kv_append calls of the new tokens;
     twopass  the long-context decode with the online softmax and with the
-             literal two-pass softmax (same algorithmic bytes; pass 1 re-reads K)."""
+             literal two-pass softmax (same algorithmic bytes; pass 1 re-reads K);
+    headbits per-KV-head sensitivity and precision assignment over the
+             long-context decode workload as the calibration set."""
     if {"sparse", "maskgen"} & set(which):
         spec = W.WORKLOADS["prefill_128k_sparse"]
         log(f"generating {spec.name}")
@@ -261,6 +263,28 @@ def bench_extras(which, torch, T, W, A):
                                                         res["online"]["us"], 3)}), flush=True)
         del k, v, q, out, ws
         torch.cuda.empty_cache()
+    if "headbits" in which:
+        spec = W.WORKLOADS["decode_128k_mixed"]
+        log(f"generating {spec.name}")
+        inp = W.make_inputs(spec)
+        kx = torch.from_numpy(inp.k).cuda()
+        vx = torch.from_numpy(inp.v).cuda()
+        q = torch.from_numpy(inp.q).cuda()
+        lens = torch.tensor(inp.structure.seq_lens, device="cuda")
+        ws = torch.empty(int(T.lib().taq_head_sensitivity_workspace_bytes(
+            spec.B, spec.Hkv, spec.Hq, spec.cap)), dtype=torch.uint8, device="cuda")
+        n_high = 2
+        scores, bits = T.head_sensitivity(kx, vx, q, lens, n_high, workspace=ws)
+        med, p10, p90 = _median_ms(torch, lambda: T.head_sensitivity(kx, vx, q, lens, n_high,
+                                                                     workspace=ws), 10)
+        fp16_bytes = 2 * kx.numel() * 2
+        print(json.dumps({"extra": "headbits", "workload": spec.name, "n_high": n_high,
+                          "ms": round(med, 3), "p10_ms": round(p10, 3), "p90_ms": round(p90, 3),
+                          "fp16_kv_bytes": int(fp16_bytes),
+                          "GB/s_of_fp16_kv": round(fp16_bytes / (med * 1e-3) / 1e9, 1),
+                          "bits": bits.cpu().tolist()}), flush=True)
+        del kx, vx, q, ws
+        torch.cuda.empty_cache()
     if "chunk" in which:
         B, Hq, Hkv, Lq, hist = 1, 32, 8, 512, 8192
         cap = hist + Lq
@@ -324,9 +348,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--only", choices=["prefill", "decode", "sparse", "maskgen", "chunk",
-                                       "twopass", "extras"], default=None,
-                    help="one leg alone; sparse / maskgen / chunk / twopass (or all four: "
-                         "extras) print their own JSON lines")
+                                       "twopass", "headbits", "extras"], default=None,
+                    help="one leg alone; sparse / maskgen / chunk / twopass / headbits (or "
+                         "all of them: extras) print their own JSON lines")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 1 GiB device copy (for HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -352,8 +376,8 @@ def main():
         return
     T.device_check(0)
 
-    if args.only in ("sparse", "maskgen", "chunk", "twopass", "extras"):
-        which = (["sparse", "maskgen", "chunk", "twopass"] if args.only == "extras"
+    if args.only in ("sparse", "maskgen", "chunk", "twopass", "headbits", "extras"):
+        which = (["sparse", "maskgen", "chunk", "twopass", "headbits"] if args.only == "extras"
                  else [args.only])
         bench_extras(which, torch, T, W, A)
         return

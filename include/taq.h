@@ -256,6 +256,36 @@ taq_status taq_tile_mask_generate(const taq_kv_cache* k_cache, const void* q_f16
                                   uint8_t* mask_out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* Workspace bytes that taq_head_sensitivity needs (0 for invalid sizes). */
+size_t taq_head_sensitivity_workspace_bytes(int32_t batch, int32_t num_kv_heads,
+                                            int32_t num_q_heads, int32_t max_seq_len);
+
+/* Per-KV-head precision assignment from measured sensitivity (section 2.4 of
+ * the block-sparse page: sensitive heads are stored at higher precision, the
+ * others with fewer bits; section 3.4: more high-precision heads, less memory
+ * saved).  The page leaves the score open; here the score of KV head g is how
+ * far its decode outputs move when its cache drops from int8 to int4:
+ *   scores[g] = sum over b, the query heads h of g and channels d of
+ *               (O4[b][h][d] - O8[b][h][d])^2,
+ * O_bits being taq_attn_decode of the calibration queries q over tokens
+ * 0 .. seq_lens[b]-1 with every head's K and V quantised at `bits` by
+ * taq_kv_quantize.  bits[g] = 8 for the n_high largest scores (ties: the lower
+ * g), 4 for the rest: a per-head bits array for taq_kv_cache.
+ * k, v: device fp16 [B][Hkv][max_seq_len][128] (calibration context); q:
+ * device fp16 [B][Hq][128]; seq_lens: device int32 [B] (clamped to
+ * [0, max_seq_len]); scores: device double [Hkv] (8-byte aligned); bits:
+ * device uint8 [Hkv]; workspace: device, 16-byte aligned, of
+ * taq_head_sensitivity_workspace_bytes() bytes (holds int8 and int4 caches,
+ * the two outputs and the decode partials).  Hq / Hkv in {1, 2, 4, 8}.
+ * Errors: INVALID_ARGUMENT (null pointer, sizes, n_high outside [0, Hkv]),
+ * UNSUPPORTED (head ratio, negative scale), MISALIGNED, WORKSPACE_TOO_SMALL. */
+taq_status taq_head_sensitivity(const void* k_f16, const void* v_f16, const void* q_f16,
+                                int32_t batch, int32_t num_kv_heads, int32_t num_q_heads,
+                                const int32_t* seq_lens, int32_t max_seq_len,
+                                float softmax_scale, int32_t n_high, double* scores,
+                                uint8_t* bits, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Test hook: when `arch` is non-NULL, taq_device_check compares this string
  * instead of the device's architecture name (NULL restores the real check). */
 void taq_debug_set_arch_override(const char* arch);

@@ -250,3 +250,38 @@ def test_tile_mask_rejects():
     if not os.path.exists("/dev/kfd"):
         assert maskgen_call(k=big, hq=1, max_len=262144)[0] == HIP   # valid: device query
         assert maskgen_call(max_len=0)[0] == HIP
+
+
+def sens_call(B=2, hkv=4, hq=8, max_len=300, n_high=1, k=FAKE, v=FAKE, q=FAKE, lens=FAKE,
+              scores=FAKE, bits=FAKE, ws=FAKE, ws_bytes=1 << 40, scale=0.0):
+    return status_of(T.lib().taq_head_sensitivity(k, v, q, B, hkv, hq, lens, max_len, scale,
+                                                  n_high, scores, bits, ws, ws_bytes, None))
+
+
+def test_head_sensitivity_workspace_bytes():
+    L = T.lib()
+    # cap 384: int8 codes 2*4*384*128 per cache, int4 half; meta 2*4*384*4 (x2 scales, x1 zeros)
+    nb = L.taq_head_sensitivity_workspace_bytes(2, 4, 8, 300)
+    c8, meta = 2 * 4 * 384 * 128, 2 * 4 * 384 * 4
+    assert nb >= 2 * c8 + 2 * (c8 // 2) + 4 * 3 * meta + 2 * 2 * 8 * 128 * 2
+    assert L.taq_head_sensitivity_workspace_bytes(0, 4, 8, 300) == 0
+    assert L.taq_head_sensitivity_workspace_bytes(2, 65, 65, 300) == 0
+
+
+def test_head_sensitivity_rejects():
+    assert sens_call(B=0)[0] == INVALID
+    assert sens_call(hkv=0)[0] == INVALID
+    assert sens_call(hq=6)[0] == INVALID
+    assert sens_call(hq=12)[0] == UNSUPPORTED            # r = 3
+    assert sens_call(max_len=-1)[0] == INVALID
+    assert sens_call(n_high=-1)[0] == INVALID
+    assert sens_call(n_high=5)[0] == INVALID
+    assert sens_call(k=0)[0] == INVALID
+    assert sens_call(bits=0)[0] == INVALID
+    assert sens_call(q=FAKE + 2)[0] == MISALIGNED
+    assert sens_call(scores=FAKE + 4)[0] == MISALIGNED
+    assert sens_call(scale=-1.0)[0] == UNSUPPORTED
+    assert sens_call(ws_bytes=16)[0] == WS_SMALL
+    assert sens_call(ws=0)[0] == WS_SMALL
+    if not os.path.exists("/dev/kfd"):
+        assert sens_call()[0] == HIP                      # valid: stops at the device query

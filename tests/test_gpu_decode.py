@@ -143,3 +143,20 @@ def test_decode_full_size_sampled(name):
         want = oa.decode(inp.q[b:b + 1, h:h + 1], kh[None, None], vh[None, None], [n])[0, 0]
         err = max_abs(got[b, h], want)
         assert err <= TOL, (b, h, err)
+
+
+def test_decode_error_scales_with_v_magnitude():
+    """The 2e-3 bar is for unit-variance data.  V-hat enters the PV product as
+    fp16, so its rounding error is relative: a V channel scaled by 2^4 keeps
+    the same relative error, i.e. at most 16x the bar in absolute terms, while
+    the other channels keep the bar."""
+    require_gpu()
+    spec = W.small("decode", B=2, Hq=8, Hkv=2, ragged=(600, 1000), bits=8, seed=41)
+    inp = W.make_inputs(spec)
+    inp.v[:, :, :, 40] = (inp.v[:, :, :, 40].astype(np.float32) * 16).astype(np.float16)
+    note("decode with a V channel x16")
+    got, want, _ = run_decode(inp)
+    err = np.abs(got - want)
+    assert err[:, :, 40].max() <= 16 * TOL
+    others = np.delete(err, 40, axis=2)
+    assert others.max() <= TOL

@@ -32,7 +32,8 @@ EXPORTS = ("taq_last_error", "taq_abi_version", "taq_device_check",
            "taq_kv_dequantize", "taq_attn_decode_workspace_bytes",
            "taq_attn_decode", "taq_attn_prefill", "taq_debug_set_arch_override",
            "taq_kv_append", "taq_attn_prefill_chunk", "taq_tile_mask_workspace_bytes",
-           "taq_tile_mask_generate", "taq_attn_decode_two_pass")
+           "taq_tile_mask_generate", "taq_attn_decode_two_pass",
+           "taq_head_sensitivity_workspace_bytes", "taq_head_sensitivity")
 
 
 class TaqError(RuntimeError):
@@ -87,6 +88,9 @@ def lib() -> ctypes.CDLL:
         "taq_kv_append": (ctypes.c_int, [CP, P, P, I32, P]),
         "taq_attn_prefill_chunk": (ctypes.c_int, [CP, CP, P, I32, I32, P, I32, MP, F, P, P]),
         "taq_tile_mask_workspace_bytes": (SZ, [CP, I32]),
+        "taq_head_sensitivity_workspace_bytes": (SZ, [I32, I32, I32, I32]),
+        "taq_head_sensitivity": (ctypes.c_int, [P, P, P, I32, I32, I32, P, I32, F, I32, P, P, P,
+                                                SZ, P]),
         "taq_tile_mask_generate": (ctypes.c_int, [CP, P, I32, P, I32, I32, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
@@ -299,3 +303,29 @@ def tile_mask_generate(k: KVCache, q, seq_lens, skip_per_mille: int, out=None, w
                                         workspace.numel() * workspace.element_size(),
                                         _stream(q.device)))
     return TileMask(out, nt, nt, stride_b=k.num_kv_heads * nt * nt, stride_h=nt * nt)
+
+
+def head_sensitivity(k, v, q, seq_lens, n_high: int, softmax_scale: float = 0.0,
+                     workspace=None):
+    """Per-KV-head sensitivity and precision: k, v fp16 [B][Hkv][S][D] (the
+    calibration context), q fp16 [B][Hq][D].  Returns (scores float64 [Hkv],
+    bits uint8 [Hkv]) as device tensors."""
+    import torch
+    for name, t, nd in (("k", k, 4), ("v", v, 4), ("q", q, 3)):
+        if t.dtype != torch.float16 or not t.is_contiguous() or t.dim() != nd:
+            raise ValueError(f"{name} must be a contiguous fp16 tensor of rank {nd}")
+    B, Hkv, S, D = k.shape
+    Hq = q.shape[1]
+    if tuple(v.shape) != tuple(k.shape) or q.shape[0] != B or q.shape[2] != D:
+        raise ValueError("k, v and q shapes do not match")
+    scores = torch.empty(Hkv, dtype=torch.float64, device=k.device)
+    bits = torch.empty(Hkv, dtype=torch.uint8, device=k.device)
+    if workspace is None:
+        nb = int(lib().taq_head_sensitivity_workspace_bytes(B, Hkv, Hq, S))
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=k.device)
+    _check(lib().taq_head_sensitivity(_ptr(k), _ptr(v), _ptr(q), B, Hkv, Hq, _ptr(seq_lens), S,
+                                      softmax_scale, int(n_high), _ptr(scores), _ptr(bits),
+                                      _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(k.device)))
+    return scores, bits

@@ -17,7 +17,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtaq.so")
-SOURCES = ["api.hip", "kv_quant.hip", "attn_decode.hip", "attn_prefill.hip", "tile_mask.hip"]
+SOURCES = ["api.hip", "kv_quant.hip", "attn_decode.hip", "attn_prefill.hip", "tile_mask.hip",
+           "head_precision.hip"]
 ARCH = "gfx950"
 
 # packed-fp32-ops is switched off for every device compile: the VOP3P packed

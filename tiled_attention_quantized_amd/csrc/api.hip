@@ -462,3 +462,146 @@ taq_status taq_tile_mask_generate(const taq_kv_cache* k, const void* q, int32_t 
 }
 
 }  // extern "C"
+
+namespace {
+
+// Workspace of taq_head_sensitivity: an int8 and an int4 copy of the K
+// (token layout) and V (channel layout) caches, the two decode outputs and one
+// decode workspace (the two decode calls run one after the other).
+struct SensPlan {
+  int cap = 0;
+  size_t k8c, k8s, k8z, v8c, v8s, v8z, k4c, k4s, k4z, v4c, v4s, v4z, o8, o4, dec, total = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+SensPlan sens_plan(int B, int Hkv, int hq, int max_len) {
+  SensPlan p;
+  p.cap = max_len > 0 ? (max_len + TAQ_TILE - 1) / TAQ_TILE * TAQ_TILE : TAQ_TILE;
+  const size_t meta = (size_t)B * Hkv * p.cap * 4;
+  const size_t c8 = (size_t)B * Hkv * p.cap * 128, c4 = c8 / 2;
+  const int chunk = taq::decode_chunk_tokens(B, Hkv, max_len);
+  const size_t nchunk = max_len > 0 ? (size_t)(max_len + chunk - 1) / chunk : 1;
+  size_t at = 0;
+  auto take = [&](size_t bytes) { const size_t o = at; at += align256(bytes); return o; };
+  p.k8c = take(c8); p.k8s = take(2 * meta); p.k8z = take(meta);
+  p.v8c = take(c8); p.v8s = take(2 * meta); p.v8z = take(meta);
+  p.k4c = take(c4); p.k4s = take(2 * meta); p.k4z = take(meta);
+  p.v4c = take(c4); p.v4s = take(2 * meta); p.v4z = take(meta);
+  p.o8 = take((size_t)B * hq * 128 * 2);
+  p.o4 = take((size_t)B * hq * 128 * 2);
+  p.dec = take((size_t)B * hq * nchunk * (128 + 2) * sizeof(float));
+  p.total = at;
+  return p;
+}
+
+taq::CacheGeom uniform_geom(uint8_t* base, size_t c, size_t sc, size_t z, int B, int H, int cap,
+                            int bits, int layout) {
+  taq::CacheGeom g;
+  std::memset(&g, 0, sizeof(g));
+  g.codes = base + c;
+  g.scales = reinterpret_cast<uint16_t*>(base + sc);
+  g.zeros = base + z;
+  const int64_t per = (int64_t)cap * 128 * bits / 8;
+  for (int h = 0; h < H; ++h) g.hoff[h] = h * per;
+  g.bstride = H * per;
+  g.is8 = bits == 8 ? (H == 64 ? ~0ull : ((1ull << H) - 1)) : 0ull;
+  g.B = B;
+  g.H = H;
+  g.D = 128;
+  g.cap = cap;
+  g.layout = layout;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t taq_head_sensitivity_workspace_bytes(int32_t batch, int32_t num_kv_heads,
+                                            int32_t num_q_heads, int32_t max_len) {
+  if (batch < 1 || num_kv_heads < 1 || num_kv_heads > TAQ_MAX_KV_HEADS || num_q_heads < 1 ||
+      max_len < 0)
+    return 0;
+  return sens_plan(batch, num_kv_heads, num_q_heads, max_len).total;
+}
+
+taq_status taq_head_sensitivity(const void* k, const void* v, const void* q, int32_t batch,
+                                int32_t hkv, int32_t hq, const int32_t* lens, int32_t max_len,
+                                float softmax_scale, int32_t n_high, double* scores,
+                                uint8_t* bits, void* ws, size_t ws_bytes, void* stream) {
+  if (batch < 1) return fail(TAQ_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+  if (hkv < 1 || hkv > TAQ_MAX_KV_HEADS)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "num_kv_heads must be in [1, %d]", TAQ_MAX_KV_HEADS);
+  if (hq < 1 || hq % hkv)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "num_q_heads (%d) must be a positive multiple of "
+                "num_kv_heads (%d)", hq, hkv);
+  const int r = hq / hkv;
+  if (r != 1 && r != 2 && r != 4 && r != 8)
+    return fail(TAQ_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads = %d (supported: 1, 2, 4, 8)", r);
+  if (max_len < 0) return fail(TAQ_ERR_INVALID_ARGUMENT, "max_seq_len must be >= 0");
+  if (n_high < 0 || n_high > hkv)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "n_high %d outside [0, num_kv_heads %d]", n_high, hkv);
+  if (!k || !v || !q || !lens || !scores || !bits)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "null k, v, q, seq_lens, scores or bits");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(q) || !aligned16(lens))
+    return fail(TAQ_ERR_MISALIGNED, "k, v, q and seq_lens must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(scores) & 7u) != 0)
+    return fail(TAQ_ERR_MISALIGNED, "scores must be 8-byte aligned");
+  if (!std::isfinite(softmax_scale))
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (softmax_scale < 0.f)
+    return fail(TAQ_ERR_UNSUPPORTED, "softmax_scale must be >= 0 (0 selects 1/sqrt(head_dim))");
+  const SensPlan p = sens_plan(batch, hkv, hq, max_len);
+  if (!ws || ws_bytes < p.total)
+    return fail(TAQ_ERR_WORKSPACE_TOO_SMALL, "workspace: need %zu bytes, got %zu", p.total,
+                ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(TAQ_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  taq_status st = device_ok();
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const taq::CacheGeom k8 = uniform_geom(w, p.k8c, p.k8s, p.k8z, batch, hkv, p.cap, 8, TAQ_LAYOUT_TOKEN);
+  const taq::CacheGeom v8 = uniform_geom(w, p.v8c, p.v8s, p.v8z, batch, hkv, p.cap, 8, TAQ_LAYOUT_CHANNEL);
+  const taq::CacheGeom k4 = uniform_geom(w, p.k4c, p.k4s, p.k4z, batch, hkv, p.cap, 4, TAQ_LAYOUT_TOKEN);
+  const taq::CacheGeom v4 = uniform_geom(w, p.v4c, p.v4s, p.v4z, batch, hkv, p.cap, 4, TAQ_LAYOUT_CHANNEL);
+  hipError_t e = hipSuccess;
+  if (max_len > 0) {
+    const taq::CacheGeom* gs[4] = {&k8, &v8, &k4, &v4};
+    const void* xs[4] = {k, v, k, v};
+    for (int i = 0; i < 4 && e == hipSuccess; ++i) {
+      taq::QuantArgs qa;
+      std::memset(&qa, 0, sizeof(qa));
+      qa.c = *gs[i];
+      qa.x = static_cast<const uint16_t*>(xs[i]);
+      qa.start = 0;
+      qa.count = max_len;
+      e = taq::launch_kv_quantize(qa, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "head_sensitivity quantise");
+  }
+  for (int pass = 0; pass < 2; ++pass) {
+    taq::DecodeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.k = pass == 0 ? k8 : k4;
+    a.v = pass == 0 ? v8 : v4;
+    a.q = static_cast<const uint16_t*>(q);
+    a.o = reinterpret_cast<uint16_t*>(w + (pass == 0 ? p.o8 : p.o4));
+    a.lens = lens;
+    a.ws = reinterpret_cast<float*>(w + p.dec);
+    a.Hq = hq;
+    a.r = r;
+    a.max_len = max_len;
+    a.chunk = taq::decode_chunk_tokens(batch, hkv, max_len);
+    a.nchunk = max_len > 0 ? (max_len + a.chunk - 1) / a.chunk : 1;
+    a.scale_log2 = scale_log2_of(softmax_scale, 128);
+    e = taq::launch_attn_decode(a, s, false);
+    if (e != hipSuccess) return hip_fail(e, "head_sensitivity decode");
+  }
+  e = taq::launch_head_assign(reinterpret_cast<const uint16_t*>(w + p.o8),
+                              reinterpret_cast<const uint16_t*>(w + p.o4), batch, hq, hkv,
+                              n_high, scores, bits, s);
+  return e == hipSuccess ? TAQ_OK : hip_fail(e, "head_sensitivity assign");
+}
+
+}  // extern "C"

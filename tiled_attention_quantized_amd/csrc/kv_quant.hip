@@ -7,9 +7,10 @@
 // rounded half to even on the exact quotients) are stated in include/taq.h.
 //
 // Exactness: an fp16 value is an integer multiple of 2^-24 below 2^41 in those
-// units, so every quantity of one group is handled as a 64-bit integer count
-// of 2^-24; each rounding is then an integer division with its remainder, and
-// no floating-point quotient ever decides a tie.
+// units; the scale is rounded up in 64-bit integer counts of 2^-24, and each
+// round-half-even quotient is decided by an exact fp32 comparison with the
+// midpoint between its two candidates (rne_quot), so no approximate quotient
+// ever decides a tie.
 #include "taq_internal.h"
 #include "device_common.h"
 
@@ -21,14 +22,6 @@ __device__ __forceinline__ int64_t f16_units(uint32_t h) {
   const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
   const int64_t mag = e == 0 ? (int64_t)m : ((int64_t)(1024u + m) << (e - 1));
   return (h & 0x8000u) ? -mag : mag;
-}
-
-// round-half-even(a / s) for a >= 0, s > 0.
-__device__ __forceinline__ uint64_t rne_div(uint64_t a, uint64_t s) {
-  uint64_t q = a / s;
-  const uint64_t r = a - q * s;
-  if (2 * r > s || (2 * r == s && (q & 1))) ++q;
-  return q;
 }
 
 // Least fp16 value >= m (m >= 1, in units of 2^-24); returns it in units and
@@ -56,6 +49,19 @@ struct GroupQ {
   uint32_t zero;
 };
 
+// round-half-even(a / s) for fp16 values 0 <= a <= 256 s, s > 0, decided
+// exactly in fp32 from an approximate quotient.  With t = floor(q) for any q
+// within 1/2 of a / s, the answer is t or t + 1 and the midpoint (t + 1/2) s
+// separates them; that product has at most 10 + 11 significant bits, so it
+// and the comparison with a are exact, ties included.  (q = a * rcp(s) is
+// within a few ulp of a / s <= 256, far inside 1/2.)
+__device__ __forceinline__ int rne_quot(float a, float s, float rs) {
+  const float t = floorf(a * rs);
+  const float mid = (t + 0.5f) * s;
+  const int n = (int)t;
+  return (a > mid || (a == mid && (n & 1))) ? n + 1 : n;
+}
+
 // Quantise the 32 fp16 values at p (16-byte aligned).
 __device__ __forceinline__ void quantize_group(const uint16_t* p, int bits,
                                                GroupQ& out) {
@@ -66,32 +72,35 @@ __device__ __forceinline__ void quantize_group(const uint16_t* p, int bits,
     const uint4 v = p4[i];
     w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
   }
-  int64_t x[32];
-  int64_t lo = 0, hi = 0;
+  float x[32];
+  float lo = 0.f, hi = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-    x[i] = f16_units(h);
-    lo = x[i] < lo ? x[i] : lo;
-    hi = x[i] > hi ? x[i] : hi;
+    x[i] = (float)bits_to_half((uint16_t)((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu));
+    lo = fminf(lo, x[i]);
+    hi = fmaxf(hi, x[i]);
   }
-  const int64_t qmax = (1 << bits) - 1;
-  const uint64_t span = (uint64_t)(hi - lo);
-  if (span == 0) {
+  const int qmax = (1 << bits) - 1;
+  if (hi == lo) {                           // all zeros (the range contains 0)
 #pragma unroll
     for (int i = 0; i < 32; ++i) out.c[i] = 0;
     out.scale_bits = 0;
     out.zero = 0;
     return;
   }
+  // the scale: least fp16 >= (hi - lo) / qmax, in integer units of 2^-24
+  const uint64_t span = (uint64_t)(f16_units(half_to_bits((_Float16)hi)) -
+                                   f16_units(half_to_bits((_Float16)lo)));
   uint32_t sb;
-  const uint64_t s = fp16_ceil((span + qmax - 1) / qmax, sb);
-  const int64_t z = (int64_t)rne_div((uint64_t)(-lo), s);
+  // (constant divisors: the compiler multiplies instead of dividing)
+  fp16_ceil(bits == 8 ? (span + 254) / 255 : (span + 14) / 15, sb);
+  const float sf = (float)bits_to_half((uint16_t)sb);
+  const float rs = __builtin_amdgcn_rcpf(sf);
+  const int z = rne_quot(-lo, sf, rs);
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const uint64_t a = (uint64_t)(x[i] < 0 ? -x[i] : x[i]);
-    const int64_t q = (int64_t)rne_div(a, s);
-    int64_t c = (x[i] < 0 ? -q : q) + z;
+    const int q = rne_quot(fabsf(x[i]), sf, rs);
+    int c = (x[i] < 0.f ? -q : q) + z;
     c = c < 0 ? 0 : (c > qmax ? qmax : c);
     out.c[i] = (uint8_t)c;
   }

@@ -75,6 +75,8 @@ struct MaskGenArgs {
 hipError_t launch_tile_mask(const MaskGenArgs& a, hipStream_t s);
 
 hipError_t launch_kv_quantize(const QuantArgs& a, hipStream_t s);
+hipError_t launch_head_assign(const uint16_t* o8, const uint16_t* o4, int B, int Hq, int Hkv,
+                              int n_high, double* scores, uint8_t* bits, hipStream_t s);
 hipError_t launch_kv_dequantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t s, bool two_pass);
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t s);
