@@ -94,7 +94,7 @@ typedef enum { TAQ_LAYOUT_TOKEN = 0, TAQ_LAYOUT_CHANNEL = 1 } taq_layout;
 typedef struct {
   int32_t batch;
   int32_t num_kv_heads;   /* 1 .. TAQ_MAX_KV_HEADS */
-  int32_t head_dim;       /* multiple of 32 */
+  int32_t head_dim;       /* multiple of 32, at most 1024 */
   int32_t group_size;     /* must be 32 */
   int32_t capacity;       /* tokens per (batch, head); multiple of 128 */
   int32_t layout;         /* taq_layout */
@@ -131,7 +131,8 @@ size_t taq_kv_meta_count(const taq_kv_cache* cache);
  * Codes, scales and zeros of other tokens are left unchanged.  Bit-exact with
  * the definition at the top of this file.  Errors: INVALID_ARGUMENT (null
  * pointer, start/count out of [0, capacity], bad shape), UNSUPPORTED (bits not
- * 4/8, group_size not 32, head_dim not a multiple of 32), MISALIGNED. */
+ * 4/8, group_size not 32, head_dim not a multiple of 32 in [32, 1024]),
+ * MISALIGNED. */
 taq_status taq_kv_quantize(const taq_kv_cache* cache, const void* x_f16,
                            int32_t start, int32_t count, void* stream);
 

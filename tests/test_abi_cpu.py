@@ -59,6 +59,7 @@ def test_sizes():
     (dict(bits=(3, 4)), UNSUPPORTED),
     (dict(group=16), UNSUPPORTED),
     (dict(D=48), UNSUPPORTED),
+    (dict(D=1056), UNSUPPORTED),
     (dict(cap=200), INVALID),
     (dict(H=0, bits=()), INVALID),
     (dict(layout=7), INVALID),

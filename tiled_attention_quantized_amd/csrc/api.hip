@@ -43,8 +43,9 @@ taq_status check_cache(const taq_kv_cache* c, const char* name, int need_layout,
                 TAQ_MAX_KV_HEADS);
   if (c->group_size != TAQ_GROUP)
     return fail(TAQ_ERR_UNSUPPORTED, "%s: group_size must be 32", name);
-  if (c->head_dim <= 0 || c->head_dim % TAQ_GROUP)
-    return fail(TAQ_ERR_UNSUPPORTED, "%s: head_dim must be a positive multiple of 32", name);
+  if (c->head_dim <= 0 || c->head_dim % TAQ_GROUP || c->head_dim > 1024)
+    return fail(TAQ_ERR_UNSUPPORTED, "%s: head_dim must be a multiple of 32 in [32, 1024]",
+                name);
   if (attention && c->head_dim != 128)
     return fail(TAQ_ERR_UNSUPPORTED, "%s: attention kernels need head_dim 128", name);
   if (c->capacity <= 0 || c->capacity % TAQ_TILE)

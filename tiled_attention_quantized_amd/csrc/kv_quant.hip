@@ -49,17 +49,19 @@ struct GroupQ {
   uint32_t zero;
 };
 
-// round-half-even(a / s) for fp16 values 0 <= a <= 256 s, s > 0, decided
-// exactly in fp32 from an approximate quotient.  With t = floor(q) for any q
-// within 1/2 of a / s, the answer is t or t + 1 and the midpoint (t + 1/2) s
-// separates them; that product has at most 10 + 11 significant bits, so it
-// and the comparison with a are exact, ties included.  (q = a * rcp(s) is
-// within a few ulp of a / s <= 256, far inside 1/2.)
+// round-half-even(a / s) for fp16 values |a| <= 256 s, s > 0, decided exactly
+// in fp32 from an approximate quotient.  With t = floor(q) for any q within
+// 1/2 of a / s, the answer is t or t + 1 and the midpoint (t + 1/2) s
+// separates them (ties go to the even one, for either sign of a); that
+// product has at most 10 + 11 significant bits, so it and the comparison with
+// a are exact.  (q = a * rcp(s) is within a few ulp of a / s, |a / s| <= 256,
+// far inside 1/2.)
 __device__ __forceinline__ int rne_quot(float a, float s, float rs) {
   const float t = floorf(a * rs);
   const float mid = (t + 0.5f) * s;
   const int n = (int)t;
-  return (a > mid || (a == mid && (n & 1))) ? n + 1 : n;
+  // branch-free: up when above the midpoint, or on it with n odd
+  return n + ((int)(a > mid) | ((int)(a == mid) & n & 1));
 }
 
 // Quantise the 32 fp16 values at p (16-byte aligned).
@@ -99,10 +101,8 @@ __device__ __forceinline__ void quantize_group(const uint16_t* p, int bits,
   const int z = rne_quot(-lo, sf, rs);
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const int q = rne_quot(fabsf(x[i]), sf, rs);
-    int c = (x[i] < 0.f ? -q : q) + z;
-    c = c < 0 ? 0 : (c > qmax ? qmax : c);
-    out.c[i] = (uint8_t)c;
+    const int c = rne_quot(x[i], sf, rs) + z;
+    out.c[i] = (uint8_t)min(max(c, 0), qmax);
   }
   out.scale_bits = sb;
   out.zero = (uint32_t)z;
@@ -112,26 +112,25 @@ __device__ __forceinline__ int head_bits(const CacheGeom& g, int h) {
   return ((g.is8 >> h) & 1ull) ? 8 : 4;
 }
 
-// Token layout: one thread per (b, h, token, group).
-__global__ void __launch_bounds__(256)
-quantize_token_kernel(QuantArgs a) {
+// Token layout: one workgroup of D threads per (b, h, 32-position block), the
+// same blocks as the channel layout; thread (t = tid / G, gi = tid % G)
+// quantises group gi of position 32 j + t when it lies in the written range
+// (append: per-batch start; positions outside the capacity are skipped).
+__global__ void __launch_bounds__(1024)
+quantize_token_kernel(QuantArgs a, int j0, int nblk) {
   const CacheGeom& g = a.c;
   const int G = g.D / 32;
-  const int64_t total = (int64_t)g.B * g.H * a.count * G;
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= total) return;
-  const int gi = (int)(id % G);
-  int64_t rest = id / G;
-  const int t = (int)(rest % a.count);
-  rest /= a.count;
-  const int h = (int)(rest % g.H);
-  const int b = (int)(rest / g.H);
+  const int jrel = blockIdx.x % nblk;
+  const int bh = blockIdx.x / nblk;
+  const int h = bh % g.H, b = bh / g.H;
+  const int start = a.starts ? a.starts[b] : a.start;
+  const int j = (a.starts ? (start >> 5) : j0) + jrel;
+  const int t = threadIdx.x / G, gi = threadIdx.x - t * G;
+  const int T = 32 * j + t;
+  if (T < start || T >= start + a.count || T < 0 || T >= g.cap) return;
   const int bits = head_bits(g, h);
-  // append: per-batch start, positions outside the capacity are skipped
-  const int T = (a.starts ? a.starts[b] : a.start) + t;
-  if (T < 0 || T >= g.cap) return;
   GroupQ q;
-  quantize_group(a.x + ((((int64_t)b * g.H + h) * a.count + t) * g.D + 32 * gi),
+  quantize_group(a.x + ((((int64_t)b * g.H + h) * a.count + (T - start)) * g.D + 32 * gi),
                  bits, q);
   uint8_t* row = g.codes + (int64_t)b * g.bstride + g.hoff[h] +
                  (int64_t)T * (g.D * bits / 8) + gi * 4 * bits;
@@ -160,66 +159,80 @@ quantize_token_kernel(QuantArgs a) {
   g.zeros[mi] = (uint8_t)q.zero;
 }
 
-// Channel layout: one thread per (b, h, group, token pair {2p, 2p+1}); both
-// tokens of a pair share their int4 bytes, so one thread owns them.
-__global__ void __launch_bounds__(256)
-quantize_channel_kernel(QuantArgs a, int p0, int npairs) {
+// Channel layout: one workgroup of D threads per (b, h, 32-token block).
+// Thread (token t = tid / G, group gi = tid % G) quantises its group (a wave
+// reads whole token rows, contiguous), writes its scale and zero-point, and
+// puts its 32 codes into an LDS copy of the block (row = channel, one byte per
+// token); thread d then writes channel row d of the block (int8: 32 bytes,
+// int4: 16 bytes, two tokens per byte), so the block goes out as contiguous
+// 16-byte stores.  Blocks cut by the ends of the written range write only
+// their tokens (an int4 byte shared with a token outside the range is
+// read, merged and written back).
+__global__ void __launch_bounds__(1024)
+quantize_channel_kernel(QuantArgs a, int j0, int nblk) {
+  extern __shared__ uint8_t cl_raw[];           // [D][36]: [channel][token] (+4: bank skew)
+  uint8_t (*cl)[36] = reinterpret_cast<uint8_t (*)[36]>(cl_raw);
   const CacheGeom& g = a.c;
   const int G = g.D / 32;
-  const int64_t total = (int64_t)g.B * g.H * G * npairs;
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= total) return;
-  int64_t rest = id / npairs;
-  const int gi = (int)(rest % G);
-  rest /= G;
-  const int h = (int)(rest % g.H);
-  const int b = (int)(rest / g.H);
-  // append: per-batch start; the pair index is relative to the start's pair
+  const int jrel = blockIdx.x % nblk;
+  const int bh = blockIdx.x / nblk;
+  const int h = bh % g.H, b = bh / g.H;
   const int start = a.starts ? a.starts[b] : a.start;
-  const int p = (a.starts ? (start >> 1) : p0) + (int)(id % npairs);
+  const int j = (a.starts ? (start >> 5) : j0) + jrel;
+  // tokens [lo, hi) of this block are written
+  const int lo = max(max(start, 32 * j), 0), hi = min(min(start + a.count, 32 * j + 32), g.cap);
+  if (lo >= hi) return;                         // whole workgroup
   const int bits = head_bits(g, h);
-  const int T0 = 2 * p;
-  const bool in0 = T0 >= start && T0 < start + a.count && T0 >= 0 && T0 < g.cap;
-  const bool in1 = T0 + 1 >= start && T0 + 1 < start + a.count && T0 + 1 >= 0 && T0 + 1 < g.cap;
-  if (!in0 && !in1) return;
-  GroupQ q0, q1;
-  const int64_t xbase = ((int64_t)b * g.H + h) * a.count;
-  if (in0) quantize_group(a.x + ((xbase + T0 - start) * g.D + 32 * gi), bits, q0);
-  if (in1) quantize_group(a.x + ((xbase + T0 + 1 - start) * g.D + 32 * gi), bits, q1);
-  const int rowb = 4 * bits;  // bytes per channel row of a 32-token block
-  uint8_t* blk = g.codes + (int64_t)b * g.bstride + g.hoff[h] +
-                 (int64_t)(T0 / 32) * g.D * rowb;
-  const int tt = T0 % 32;
-#pragma unroll 4
-  for (int i = 0; i < 32; ++i) {
-    uint8_t* row = blk + (int64_t)(32 * gi + i) * rowb;
-    if (bits == 8) {
-      if (in0 && in1) {
-        *reinterpret_cast<uint16_t*>(row + tt) = (uint16_t)(q0.c[i] | (q1.c[i] << 8));
-      } else if (in0) {
-        row[tt] = q0.c[i];
-      } else if (in1) {
-        row[tt + 1] = q1.c[i];
-      }
+  const int tid = threadIdx.x;
+  const int t = tid / G, gi = tid - t * G;
+  const int T = 32 * j + t;
+  if (T >= lo && T < hi) {
+    GroupQ q;
+    quantize_group(a.x + (((int64_t)b * g.H + h) * a.count + (T - start)) * g.D + 32 * gi, bits,
+                   q);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) cl[32 * gi + i][t] = q.c[i];
+    const int64_t mi = (((int64_t)b * g.H + h) * G + gi) * g.cap + T;
+    g.scales[mi] = (uint16_t)q.scale_bits;
+    g.zeros[mi] = (uint8_t)q.zero;
+  }
+  __syncthreads();
+  const int d = tid;                             // channel row
+  const int rowb = 4 * bits;
+  uint8_t* row = g.codes + (int64_t)b * g.bstride + g.hoff[h] + ((int64_t)j * g.D + d) * rowb;
+  const int t0 = lo - 32 * j, t1 = hi - 32 * j;
+  if (bits == 8) {
+    if (t0 == 0 && t1 == 32) {
+      u32x4 w[2];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        w[k >> 2][k & 3] = cl[d][4 * k] | (cl[d][4 * k + 1] << 8) | (cl[d][4 * k + 2] << 16) |
+                           ((uint32_t)cl[d][4 * k + 3] << 24);
+      reinterpret_cast<u32x4*>(row)[0] = w[0];
+      reinterpret_cast<u32x4*>(row)[1] = w[1];
     } else {
-      uint8_t* bp = row + tt / 2;
-      if (in0 && in1) {
-        *bp = (uint8_t)(q0.c[i] | (q1.c[i] << 4));
-      } else if (in0) {
-        *bp = (uint8_t)((*bp & 0xF0) | q0.c[i]);
-      } else if (in1) {
-        *bp = (uint8_t)((*bp & 0x0F) | (q1.c[i] << 4));
+      for (int k = t0; k < t1; ++k) row[k] = cl[d][k];
+    }
+  } else {
+    if (t0 == 0 && t1 == 32) {
+      u32x4 w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v |= (uint32_t)cl[d][8 * k + e] << (4 * e);
+        w[k] = v;
+      }
+      *reinterpret_cast<u32x4*>(row) = w;
+    } else {
+      for (int k = t0 >> 1; k <= (t1 - 1) >> 1; ++k) {
+        const bool in0 = 2 * k >= t0, in1 = 2 * k + 1 < t1;
+        uint8_t v = row[k];
+        if (in0) v = (uint8_t)((v & 0xF0) | cl[d][2 * k]);
+        if (in1) v = (uint8_t)((v & 0x0F) | (cl[d][2 * k + 1] << 4));
+        row[k] = v;
       }
     }
-  }
-  const int64_t mrow = (((int64_t)b * g.H + h) * G + gi) * g.cap;
-  if (in0) {
-    g.scales[mrow + T0] = (uint16_t)q0.scale_bits;
-    g.zeros[mrow + T0] = (uint8_t)q0.zero;
-  }
-  if (in1) {
-    g.scales[mrow + T0 + 1] = (uint16_t)q1.scale_bits;
-    g.zeros[mrow + T0 + 1] = (uint8_t)q1.zero;
   }
 }
 
@@ -270,19 +283,17 @@ inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1)
 }  // namespace
 
 hipError_t launch_kv_quantize(const QuantArgs& a, hipStream_t s) {
-  const int G = a.c.D / 32;
   if (a.count == 0) return hipSuccess;
-  if (a.c.layout == TAQ_LAYOUT_TOKEN) {
-    const int64_t n = (int64_t)a.c.B * a.c.H * a.count * G;
-    hipLaunchKernelGGL(quantize_token_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s, a);
-  } else {
-    // per-batch starts: up to count / 2 + 1 pairs from each start's pair
-    const int p0 = a.starts ? 0 : a.start / 2;
-    const int np = a.starts ? a.count / 2 + 1 : (a.start + a.count - 1) / 2 - p0 + 1;
-    const int64_t n = (int64_t)a.c.B * a.c.H * G * np;
-    hipLaunchKernelGGL(quantize_channel_kernel, dim3(blocks_for(n, 256)), dim3(256), 0, s,
-                       a, p0, np);
-  }
+  // 32-position blocks: the range's own, or (per-batch starts) enough blocks
+  // from each start's block to cover count tokens at any alignment
+  const int j0 = a.starts ? 0 : a.start / 32;
+  const int nblk = a.starts ? a.count / 32 + 2 : (a.start + a.count - 1) / 32 - j0 + 1;
+  const int64_t n = (int64_t)a.c.B * a.c.H * nblk;
+  if (a.c.layout == TAQ_LAYOUT_TOKEN)
+    hipLaunchKernelGGL(quantize_token_kernel, dim3((unsigned)n), dim3(a.c.D), 0, s, a, j0, nblk);
+  else
+    hipLaunchKernelGGL(quantize_channel_kernel, dim3((unsigned)n), dim3(a.c.D), a.c.D * 36, s, a,
+                       j0, nblk);
   return hipGetLastError();
 }
 
