@@ -32,9 +32,11 @@
 //    applies the 4 group scales itself: score = sum_g s_g * dot_g.
 //  * PV: A = V-hat^T (rows = channels) dequantised to fp16 in registers from
 //    the channel-major V layout (8 consecutive tokens of one channel per lane;
-//    a lane's 8 channels 8*i16 .. +7 share one quantisation group, so it needs
-//    one group's scales and zeros), B = P^T gathered across lanes with
-//    ds_bpermute; O^T accumulates in fp32.
+//    the 16 lanes of a row read 16 consecutive channel rows, so each load
+//    instruction is one contiguous run; the scales and zeros of the 8 tokens
+//    come per quantisation group from one lane of the row by a DPP
+//    broadcast), B = P^T gathered across lanes with ds_bpermute; O^T
+//    accumulates in fp32.
 #include "taq_internal.h"
 #include "device_common.h"
 
@@ -88,9 +90,9 @@ struct StepData {
   u32x4 kc[2][2];   // K codes of the lane's two tokens (group lg); int4 uses [bk][0]
   uint32_t kz[2];   // K zero bytes of those tokens (group lg)
   u32x2 ks[2];      // K scales of those tokens (all 4 groups)
-  u32x2 vc[8];      // V codes: channel 8*i16 + db, tokens 8*lg .. +7 (int4: vc[db][0])
-  u32x2 vz;         // V zeros of the lane's 8 tokens (group i16 / 4)
-  u32x4 vs;         // V scales of the lane's 8 tokens (group i16 / 4)
+  u32x2 vc[8];      // V codes: channel 16*db + i16, tokens 8*lg .. +7 (int4: vc[db][0])
+  u32x2 vz;         // V zeros of the lane's 8 tokens (group i16 % 4)
+  u32x4 vs;         // V scales of the lane's 8 tokens (group i16 % 4)
 };
 
 struct Ptrs {
@@ -121,11 +123,12 @@ __device__ __forceinline__ void load_step(const Ptrs& p, int t0, int i16, int lg
     s.kz[bk] = p.kzero[T * 4 + lg];
     s.ks[bk] = *reinterpret_cast<const u32x2*>(p.kscale + T * 4);
   }
-  // one V block of D channel rows per step
+  // one V block of D channel rows per step; load db covers rows 16 db .. +15,
+  // one contiguous 256 (int4) / 512 (int8) byte run per instruction
   const uint8_t* vblk = p.vbase + (uint32_t)(t0 >> 5) * (uint32_t)(D * (V8 ? 32 : 16));
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
-    const uint32_t d = 8 * i16 + db;
+    const uint32_t d = 16 * db + i16;
     if (V8) {
       s.vc[db] = *reinterpret_cast<const u32x2*>(vblk + (d * 32 + 8 * lg));
     } else {
@@ -133,7 +136,9 @@ __device__ __forceinline__ void load_step(const Ptrs& p, int t0, int i16, int lg
       s.vc[db][1] = 0u;
     }
   }
-  const uint32_t mo = (uint32_t)(i16 >> 2) * (uint32_t)p.cap + (uint32_t)(t0 + 8 * lg);
+  // lanes i16 = 0..3 of each row hold the row's tokens' scales and zeros of
+  // groups 0..3 (the other lanes repeat them); compute_step broadcasts them
+  const uint32_t mo = (uint32_t)(i16 & 3) * (uint32_t)p.cap + (uint32_t)(t0 + 8 * lg);
   s.vz = *reinterpret_cast<const u32x2*>(p.vzero + mo);
   s.vs = *reinterpret_cast<const u32x4*>(p.vscale + mo);
 }
@@ -145,6 +150,41 @@ struct WaveState {
   float m_run[NRB], l_run[NRB];
   f32x4 acc[8];
 };
+
+// Lane N of each 16-lane row copied to the whole row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + N, 0xF, 0xF, false);
+}
+
+// PV for the two V loads of quantisation group GQ: that group's scales and
+// zero-points of the row's 8 tokens come from lane GQ of the row.
+template <bool V8, int GQ>
+__device__ __forceinline__ void pv_group(f32x4 (&acc)[8], const StepData& s, half8 bp,
+                                         const uint32_t (&keep)[4]) {
+  u32x2 z;
+  u32x4 sc;
+  z[0] = row_bcast<GQ>(s.vz[0]);
+  z[1] = row_bcast<GQ>(s.vz[1]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sc[j] = row_bcast<GQ>(s.vs[j]) & keep[j];
+  uint32_t nzp[4], scp[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    nzp[m] = v_negz_pair<V8>(z, m);
+    scp[m] = v_scale_pair<V8>(sc, m);
+  }
+#pragma unroll
+  for (int db = 2 * GQ; db < 2 * GQ + 2; ++db) {
+    u32x4 o;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const half2v cz = u32_to_h2(v_code_pair<V8>(s.vc[db], m)) + u32_to_h2(nzp[m]);
+      o[m] = h2_to_u32(cz * u32_to_h2(scp[m]));
+    }
+    acc[db] = mfma16x16x32(u4_to_h8(o), bp, acc[db]);
+  }
+}
 
 template <int R, bool K8, bool V8, int MODE>
 __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K8, V8>& ws,
@@ -270,28 +310,17 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
   // ---------------- V-hat^T operand and PV ----------------
   // zero the scales of tokens past the end so their V-hat is exactly 0
   // (branch-free selects: no divergent control flow inside the step)
+  uint32_t keep[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int ta = 8 * lg + 2 * j;
-    const uint32_t keep = (ta < nvalid ? 0x0000FFFFu : 0u) | (ta + 1 < nvalid ? 0xFFFF0000u : 0u);
-    s.vs[j] &= keep;
+    keep[j] = (ta < nvalid ? 0x0000FFFFu : 0u) | (ta + 1 < nvalid ? 0xFFFF0000u : 0u);
   }
-  uint32_t nzp[4], scp[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    nzp[m] = v_negz_pair<V8>(s.vz, m);
-    scp[m] = v_scale_pair<V8>(s.vs, m);
-  }
-#pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    u32x4 o;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const half2v cz = u32_to_h2(v_code_pair<V8>(s.vc[db], m)) + u32_to_h2(nzp[m]);
-      o[m] = h2_to_u32(cz * u32_to_h2(scp[m]));
-    }
-    ws.acc[db] = mfma16x16x32(u4_to_h8(o), bp, ws.acc[db]);
-  }
+  // loads 2 gq and 2 gq + 1 are channels of group gq
+  pv_group<V8, 0>(ws.acc, s, bp, keep);
+  pv_group<V8, 1>(ws.acc, s, bp, keep);
+  pv_group<V8, 2>(ws.acc, s, bp, keep);
+  pv_group<V8, 3>(ws.acc, s, bp, keep);
 }
 
 template <int R, bool K8, bool V8, int MODE>
@@ -391,23 +420,25 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
   // computed.  Every iteration issues exactly one step of loads (past the end:
   // a repeat of a valid step that is never used), so the number of loads in
   // flight is the same on every path and each wait before a use is partial.
+  // (A third buffer for the int4 variant measured no faster.)
+  auto addr = [&](int t) { return t < t_end ? t : t_safe; };
   StepData A, Bf;
   int t_cur = next_step(t_begin);
   if (t_cur < t_end) {
     load_step<K8, V8>(p, t_cur, i16, lg, A);
     int t_nxt = next_step(t_cur + STEP);
-    load_step<K8, V8>(p, t_nxt < t_end ? t_nxt : t_safe, i16, lg, Bf);
+    load_step<K8, V8>(p, addr(t_nxt), i16, lg, Bf);
     while (true) {
       compute_step<R, K8, V8, MODE>(a, ws, A, t_end - t_cur, i16, lg);
       t_cur = t_nxt;
       if (t_cur >= t_end) break;
       t_nxt = next_step(t_cur + STEP);
-      load_step<K8, V8>(p, t_nxt < t_end ? t_nxt : t_safe, i16, lg, A);
+      load_step<K8, V8>(p, addr(t_nxt), i16, lg, A);
       compute_step<R, K8, V8, MODE>(a, ws, Bf, t_end - t_cur, i16, lg);
       t_cur = t_nxt;
       if (t_cur >= t_end) break;
       t_nxt = next_step(t_cur + STEP);
-      load_step<K8, V8>(p, t_nxt < t_end ? t_nxt : t_safe, i16, lg, Bf);
+      load_step<K8, V8>(p, addr(t_nxt), i16, lg, Bf);
     }
   }
 
@@ -446,7 +477,7 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
     for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        so[(w * R + i16) * D + 32 * lg + 8 * v + db] = ws.acc[db][v];
+        so[(w * R + i16) * D + 16 * db + 4 * lg + v] = ws.acc[db][v];
   }
   __syncthreads();
   const int nchunk = a.nchunk;
@@ -472,12 +503,11 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
   }
 }
 
-#ifndef TAQ_DECODE_WAVES_INT4
-#define TAQ_DECODE_WAVES_INT4 3
-#endif
+// Two waves per SIMD for every variant: the register budget that leaves
+// (up to 256 VGPRs) holds two steps of loads without spilling; at three waves
+// the int4 variant spilled and ran 20% slower.
 template <int R, bool K8, bool V8, int MODE>
-__global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu((K8 || V8) ? 2 : TAQ_DECODE_WAVES_INT4, (K8 || V8) ? 2 : TAQ_DECODE_WAVES_INT4)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_split_kernel(DecodeArgs a) {
   __shared__ float lds[2 * WAVES * R + WAVES * R * D];
   const int units = a.k.B * a.nheads;
