@@ -526,46 +526,53 @@ decode_split_kernel(DecodeArgs a) {
   decode_body<R, K8, V8, MODE>(a, b, g, c, n, lds);
 }
 
-// One wave per (batch, query head): lanes own chunks for the max / normaliser
-// and channel pairs (2 * lane, 2 * lane + 1) for the accumulator.  TWO_PASS:
-// every chunk's partials are relative to the same global maximum, so they add.
+// One workgroup per (batch, query head).  Every wave finds the global maximum
+// over all chunks (lanes over chunks); wave w then adds chunks w, w + 4, ...
+// (lane = channel pair) and the four partials are added in wave order, so the
+// result is repeatable.  TWO_PASS: every chunk's partials are relative to the
+// same global maximum, so they add with factor 1.
 template <bool TWO_PASS>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(DecodeArgs a) {
+  __shared__ float po[WAVES][D];
+  __shared__ float pl[WAVES];
   const int lane = threadIdx.x & 63;
-  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (bh >= a.k.B * a.Hq) return;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int bh = blockIdx.x;
   const int b = bh / a.Hq;
   int n = a.lens[b];
   n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
   const int nc = (n + a.chunk - 1) / a.chunk;
   const float* src = a.ws + (int64_t)bh * a.nchunk * (D + 2);
   float M = NEG_BIG;
-  for (int c = lane; c < nc; c += 64) M = fmaxf(M, src[(int64_t)c * (D + 2)]);
-  M = fmaxf(M, __shfl_xor(M, 32));
-  M = row16_max(fmaxf(M, __shfl_xor(M, 16)));
-  float l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int c0 = 0; c0 < nc; c0 += 64) {
-    const int c = c0 + lane;
-    float f = 0.f;
-    if (c < nc) {
-      f = TWO_PASS ? 1.f : fast_exp2(src[(int64_t)c * (D + 2)] - M);
-      l = fmaf(src[(int64_t)c * (D + 2) + 1], f, l);
-    }
-    const int cn = min(64, nc - c0);
-#pragma unroll 8
-    for (int j = 0; j < cn; ++j) {
-      const float fj = __shfl(f, j);
-      const float2 v = *reinterpret_cast<const float2*>(src + (int64_t)(c0 + j) * (D + 2) + 2 + 2 * lane);
-      o0 = fmaf(v.x, fj, o0);
-      o1 = fmaf(v.y, fj, o1);
-    }
+  if (!TWO_PASS) {
+    for (int c = lane; c < nc; c += 64) M = fmaxf(M, src[(int64_t)c * (D + 2)]);
+    M = fmaxf(M, __shfl_xor(M, 32));
+    M = row16_max(fmaxf(M, __shfl_xor(M, 16)));
   }
-  l += __shfl_xor(l, 32);
-  l = row16_sum(l + __shfl_xor(l, 16));
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  half2v h = {(_Float16)(o0 * inv), (_Float16)(o1 * inv)};
-  *reinterpret_cast<half2v*>(a.o + (int64_t)bh * D + 2 * lane) = h;
+  float l = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll 4
+  for (int c = w; c < nc; c += WAVES) {
+    const float* cs = src + (int64_t)c * (D + 2);
+    const float f = TWO_PASS ? 1.f : fast_exp2(cs[0] - M);
+    l = fmaf(cs[1], f, l);
+    const float2 v = *reinterpret_cast<const float2*>(cs + 2 + 2 * lane);
+    o0 = fmaf(v.x, f, o0);
+    o1 = fmaf(v.y, f, o1);
+  }
+  po[w][2 * lane] = o0;
+  po[w][2 * lane + 1] = o1;
+  if (lane == 0) pl[w] = l;
+  __syncthreads();
+  if (w == 0) {
+    const float L = ((pl[0] + pl[1]) + pl[2]) + pl[3];
+    const float O0 = ((po[0][2 * lane] + po[1][2 * lane]) + po[2][2 * lane]) + po[3][2 * lane];
+    const float O1 = ((po[0][2 * lane + 1] + po[1][2 * lane + 1]) + po[2][2 * lane + 1]) +
+                     po[3][2 * lane + 1];
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    half2v h = {(_Float16)(O0 * inv), (_Float16)(O1 * inv)};
+    *reinterpret_cast<half2v*>(a.o + (int64_t)bh * D + 2 * lane) = h;
+  }
 }
 
 }  // namespace
@@ -624,9 +631,9 @@ hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t s, bool two_pass)
   if (e != hipSuccess) return e;
   const int nbh = a.k.B * a.Hq;
   if (two_pass)
-    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3((nbh + 3) / 4), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(nbh), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3((nbh + 3) / 4), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(nbh), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
