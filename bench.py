@@ -301,16 +301,19 @@ def bench_extras(which, torch, T, W, A):
         xk = torch.from_numpy(np.ascontiguousarray(kv.k[:, :, hist:])).cuda()
         xv = torch.from_numpy(np.ascontiguousarray(kv.v[:, :, hist:])).cuda()
         flops = 4 * 128 * Hq * sum(hist + i + 1 for i in range(Lq))
-        med, _, _ = _median_ms(torch, lambda: T.attn_prefill_chunk(k, v, q, lens, cap, out=out),
-                               20)
+        nb = T.prefill_chunk_workspace_bytes(k, Hq, Lq, cap)
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+        med, _, _ = _median_ms(torch, lambda: T.attn_prefill_chunk(k, v, q, lens, cap, out=out,
+                                                                   workspace=ws), 20)
 
         def with_append():
             T.kv_append(k, xk, starts)
             T.kv_append(v, xv, starts)
-            T.attn_prefill_chunk(k, v, q, lens, cap, out=out)
+            T.attn_prefill_chunk(k, v, q, lens, cap, out=out, workspace=ws)
         med2, _, _ = _median_ms(torch, with_append, 20)
         tf = flops / (med * 1e-3) / 1e12
         print(json.dumps({"extra": "chunk", "workload": f"chunk {Lq} rows after {hist} cached",
+                          "key_splits_workspace_bytes": int(nb),
                           "ms": round(med, 4), "ms_with_append": round(med2, 4),
                           "flops": int(flops), "TFLOP/s": round(tf, 1),
                           "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}), flush=True)

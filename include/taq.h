@@ -202,6 +202,12 @@ taq_status taq_attn_prefill(const taq_kv_cache* k_cache,
                             int32_t max_seq_len, const taq_tile_mask* mask,
                             float softmax_scale, void* o_f16, void* stream);
 
+/* Workspace bytes that taq_attn_prefill_chunk can use for these shapes (0 when
+ * it would not split the key range, or for invalid sizes). */
+size_t taq_attn_prefill_chunk_workspace_bytes(const taq_kv_cache* k_cache,
+                                              int32_t num_q_heads, int32_t q_len,
+                                              int32_t max_seq_len);
+
 /* Chunked prefill against an existing cache: q/o [B][Hq][q_len][D] are the
  * last q_len positions of each sequence, whose keys and values are already
  * in the cache (append them first with taq_kv_append), so row i of batch b
@@ -210,15 +216,21 @@ taq_status taq_attn_prefill(const taq_kv_cache* k_cache,
  * positions; rows with p < 0 are written as zeros.  This is the step of the
  * multi-turn setting that section 4.2 of the KV-quantisation page discusses:
  * a new turn reads the quantised history through the same tiled kernel.
- * q_len must lie in
- * [0, max_seq_len]; everything else as taq_attn_prefill, which is the case
- * q_len = max_seq_len with every seq_lens[b] = max_seq_len. */
+ * q_len must lie in [0, max_seq_len]; everything else as taq_attn_prefill,
+ * which is the case q_len = max_seq_len with every seq_lens[b] =
+ * max_seq_len.  A short chunk has few query blocks, so with a workspace
+ * (device, 16-byte aligned, at least taq_attn_prefill_chunk_workspace_bytes())
+ * the key range of each block is split over several workgroups whose partial
+ * (max, normaliser, accumulator) triples are merged in a second kernel in
+ * split order; workspace = NULL (bytes ignored) runs unsplit.  Errors: as
+ * taq_attn_prefill, plus WORKSPACE_TOO_SMALL and MISALIGNED (workspace). */
 taq_status taq_attn_prefill_chunk(const taq_kv_cache* k_cache,
                                   const taq_kv_cache* v_cache, const void* q_f16,
                                   int32_t num_q_heads, int32_t q_len,
                                   const int32_t* seq_lens, int32_t max_seq_len,
                                   const taq_tile_mask* mask, float softmax_scale,
-                                  void* o_f16, void* stream);
+                                  void* o_f16, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* Workspace bytes that taq_tile_mask_generate needs (0 for an invalid
  * descriptor or max_seq_len). */

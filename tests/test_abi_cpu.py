@@ -171,12 +171,13 @@ def test_arch_override_rejects_other_gpus():
 
 
 def chunk_call(k=None, v=None, hq=8, q_len=64, max_len=200, mask=None, q=FAKE, o=FAKE,
-               lens=FAKE, scale=0.0):
+               lens=FAKE, scale=0.0, ws=None, ws_bytes=0):
     k = k or cache(B=1, H=2, cap=256, bits=(8, 8), layout=0)
     v = v or cache(B=1, H=2, cap=256, bits=(8, 8), layout=1)
     m = ctypes.byref(mask) if mask is not None else None
     return status_of(T.lib().taq_attn_prefill_chunk(ctypes.byref(k), ctypes.byref(v), q, hq,
-                                                    q_len, lens, max_len, m, scale, o, None))
+                                                    q_len, lens, max_len, m, scale, o, ws,
+                                                    ws_bytes, None))
 
 
 def test_chunk_prefill_rejects():
@@ -191,9 +192,20 @@ def test_chunk_prefill_rejects():
     # its own: q_len within [0, max_seq_len]
     assert chunk_call(q_len=201)[0] == INVALID
     assert chunk_call(q_len=-1)[0] == INVALID
+    # the optional key-range split workspace
+    k = cache(B=1, H=2, cap=8704, bits=(8, 8), layout=0)
+    v = cache(B=1, H=2, cap=8704, bits=(8, 8), layout=1)
+    nb = T.lib().taq_attn_prefill_chunk_workspace_bytes(ctypes.byref(k), 8, 512, 8704)
+    assert nb > 0 and nb % (132 * 4) == 0             # [splits][B][Hq][q_len][D + 4] floats
+    # a whole-sequence-sized chunk over 8 KV heads has workgroups enough: no split
+    k8 = cache(B=1, H=8, cap=8704, bits=(8,) * 8, layout=0)
+    assert T.lib().taq_attn_prefill_chunk_workspace_bytes(ctypes.byref(k8), 32, 8704, 8704) == 0
+    assert chunk_call(k=k, v=v, q_len=512, max_len=8704, ws=FAKE, ws_bytes=nb - 1)[0] == WS_SMALL
+    assert chunk_call(k=k, v=v, q_len=512, max_len=8704, ws=FAKE + 8, ws_bytes=nb)[0] == MISALIGNED
     if not os.path.exists("/dev/kfd"):
         assert chunk_call(q_len=0)[0] == HIP          # valid: stops at the device query
         assert chunk_call(q_len=200)[0] == HIP
+        assert chunk_call(k=k, v=v, q_len=512, max_len=8704, ws=FAKE, ws_bytes=nb)[0] == HIP
 
 
 def test_kv_append_rejects():

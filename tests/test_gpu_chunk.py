@@ -20,8 +20,10 @@ pytestmark = pytest.mark.gpu
 
 
 def _mask_tensor(mask):
+    """[nq][nk] (shared) or [B][nq][nk] (per batch entry) keep-mask."""
     md = torch.from_numpy(np.ascontiguousarray(mask)).cuda()
-    return T.TileMask(md, mask.shape[-2], mask.shape[-1])
+    sb = mask.shape[-2] * mask.shape[-1] if mask.ndim == 3 else 0
+    return T.TileMask(md, mask.shape[-2], mask.shape[-1], stride_b=sb)
 
 
 @pytest.mark.parametrize("layout", ["token", "channel"])
@@ -46,7 +48,8 @@ def test_kv_append_bytes(layout):
     assert_cache_equal(gc, oc)
 
 
-def _chunk_case(r, Lq, lens, cap, mask=None, seed=0, bits=8, n_int8=0):
+def _chunk_case(r, Lq, lens, cap, mask=None, seed=0, bits=8, n_int8=0, workspace="auto",
+                also_unsplit=False):
     Hkv = 2 if r < 8 else 1
     Hq = Hkv * r
     B = len(lens)
@@ -59,9 +62,14 @@ def _chunk_case(r, Lq, lens, cap, mask=None, seed=0, bits=8, n_int8=0):
     vc = gpu_cache(kv.v, hb, T.LAYOUT_CHANNEL, cap)
     tm = _mask_tensor(mask) if mask is not None else None
     out = T.attn_prefill_chunk(kc, vc, torch.from_numpy(q).cuda(), lens_tensor(lens), cap,
-                               mask=tm)
+                               mask=tm, workspace=workspace)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
+    if also_unsplit:
+        one = T.attn_prefill_chunk(kc, vc, torch.from_numpy(q).cuda(), lens_tensor(lens), cap,
+                                   mask=tm, workspace=None)
+        torch.cuda.synchronize()
+        got = (got, one.cpu().numpy().astype(np.float64))
     okc = oq.build_cache(kv.k, hb, "token", cap=cap)
     ovc = oq.build_cache(kv.v, hb, "channel", cap=cap)
     want = oa.prefill_chunk(q, oq.dequantized_all(okc), oq.dequantized_all(ovc), lens,
@@ -158,3 +166,26 @@ def test_chunk_long_history_sampled_rows():
                             rows=rows, heads=heads, workers=8)
     err = max(max_abs(got[0, h][rows], want[0, h]) for _, h in heads)
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("r", [1, 4, 8])
+def test_chunk_key_range_split(r):
+    """Short chunks over a long history split each query block's key range
+    over several workgroups (partials merged in split order): ragged lengths,
+    a sequence shorter than the chunk (padding rows, empty splits) and a mask,
+    against the oracle and against the unsplit kernel."""
+    require_gpu()
+    cap, Lq = 2048, 100
+    lens = np.array([2048, 1500, 60, 700], dtype=np.int32)
+    Hkv = 2 if r < 8 else 1
+    kd = T.KVCache(4, Hkv, 128, cap, [8] * Hkv, T.LAYOUT_TOKEN)
+    assert T.prefill_chunk_workspace_bytes(kd, Hkv * r, Lq, cap) > 0     # the split is taken
+    nt = cap // 128
+    mask = np.tril(np.ones((4, nt, nt), np.uint8))
+    mask[0, 15, 3:9] = 0
+    mask[1, 11, 1:4] = 0
+    note(f"chunk split r={r} lens={lens.tolist()}")
+    (got, one), want = _chunk_case(r, Lq, lens, cap, mask=mask, seed=500 + r, also_unsplit=True)
+    assert max_abs(got, want) <= TOL
+    assert max_abs(got, one) <= TOL
+    assert not got[2, :, :Lq - 60].any()          # rows at negative positions

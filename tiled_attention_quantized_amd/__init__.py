@@ -33,7 +33,8 @@ EXPORTS = ("taq_last_error", "taq_abi_version", "taq_device_check",
            "taq_attn_decode", "taq_attn_prefill", "taq_debug_set_arch_override",
            "taq_kv_append", "taq_attn_prefill_chunk", "taq_tile_mask_workspace_bytes",
            "taq_tile_mask_generate", "taq_attn_decode_two_pass",
-           "taq_head_sensitivity_workspace_bytes", "taq_head_sensitivity")
+           "taq_head_sensitivity_workspace_bytes", "taq_head_sensitivity",
+           "taq_attn_prefill_chunk_workspace_bytes")
 
 
 class TaqError(RuntimeError):
@@ -86,7 +87,9 @@ def lib() -> ctypes.CDLL:
         "taq_attn_prefill": (ctypes.c_int, [CP, CP, P, I32, P, I32, MP, F, P, P]),
         "taq_debug_set_arch_override": (None, [ctypes.c_char_p]),
         "taq_kv_append": (ctypes.c_int, [CP, P, P, I32, P]),
-        "taq_attn_prefill_chunk": (ctypes.c_int, [CP, CP, P, I32, I32, P, I32, MP, F, P, P]),
+        "taq_attn_prefill_chunk": (ctypes.c_int, [CP, CP, P, I32, I32, P, I32, MP, F, P, P, SZ,
+                                                  P]),
+        "taq_attn_prefill_chunk_workspace_bytes": (SZ, [CP, I32, I32, I32]),
         "taq_tile_mask_workspace_bytes": (SZ, [CP, I32]),
         "taq_head_sensitivity_workspace_bytes": (SZ, [I32, I32, I32, I32]),
         "taq_head_sensitivity": (ctypes.c_int, [P, P, P, I32, I32, I32, P, I32, F, I32, P, P, P,
@@ -256,22 +259,36 @@ def attn_prefill(k: KVCache, v: KVCache, q, seq_lens, mask: Optional[TileMask] =
     return out
 
 
+def prefill_chunk_workspace_bytes(k: KVCache, num_q_heads: int, q_len: int,
+                                  max_seq_len: int) -> int:
+    d = k.desc()
+    return int(lib().taq_attn_prefill_chunk_workspace_bytes(ctypes.byref(d), num_q_heads, q_len,
+                                                            max_seq_len))
+
+
 def attn_prefill_chunk(k: KVCache, v: KVCache, q, seq_lens, max_seq_len: int,
                        mask: Optional[TileMask] = None, softmax_scale: float = 0.0,
-                       out=None):
+                       out=None, workspace="auto"):
     """Chunked prefill: q fp16 [B][Hq][Lq][D] holds the last Lq positions of each
     sequence (already appended to the cache); row i of batch b sits at
-    position seq_lens[b] - Lq + i."""
+    position seq_lens[b] - Lq + i.  workspace: "auto" allocates the key-range
+    split workspace the library asks for, None runs unsplit, or a device
+    uint8 tensor."""
     import torch
     B, Hq, Lq, D = q.shape
     if out is None:
         out = torch.empty_like(q)
+    if isinstance(workspace, str):
+        nb = prefill_chunk_workspace_bytes(k, Hq, Lq, max_seq_len)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
     kd, vd = k.desc(), v.desc()
     md = mask.desc() if mask is not None else None
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().taq_attn_prefill_chunk(ctypes.byref(kd), ctypes.byref(vd), _ptr(q), Hq, Lq,
                                         _ptr(seq_lens), max_seq_len,
                                         ctypes.byref(md) if md is not None else None,
-                                        softmax_scale, _ptr(out), _stream(q.device)))
+                                        softmax_scale, _ptr(out), _ptr(workspace), nbytes,
+                                        _stream(q.device)))
     return out
 
 

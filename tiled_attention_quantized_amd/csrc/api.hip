@@ -309,10 +309,14 @@ namespace {
 
 // Shared body of taq_attn_prefill (q_len = max_len, chunk = false) and
 // taq_attn_prefill_chunk.
+size_t prefill_part_bytes(int nsplit, int B, int hq, int q_len) {
+  return nsplit > 1 ? (size_t)nsplit * B * hq * q_len * (128 + 4) * sizeof(float) : 0;
+}
+
 taq_status prefill_common(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
                           int32_t hq, int32_t q_len, bool chunk, const int32_t* lens,
                           int32_t max_len, const taq_tile_mask* mask, float softmax_scale,
-                          void* o, void* stream) {
+                          void* o, void* ws, size_t ws_bytes, void* stream) {
   taq_status st = check_pair(k, v, hq, max_len);
   if (st) return st;
   if (q_len < 0 || q_len > max_len)
@@ -327,6 +331,16 @@ taq_status prefill_common(const taq_kv_cache* k, const taq_kv_cache* v, const vo
   const int nt = (max_len + TAQ_TILE - 1) / TAQ_TILE;
   st = check_mask(mask, nt, nt);
   if (st) return st;
+  // key-range splits when a workspace is given (chunked prefill)
+  int nsplit = 1;
+  if (ws) {
+    if (!aligned16(ws)) return fail(TAQ_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+    nsplit = taq::prefill_splits(k->batch, k->num_kv_heads, hq / k->num_kv_heads, q_len, max_len);
+    const size_t need = prefill_part_bytes(nsplit, k->batch, hq, q_len);
+    if (ws_bytes < need)
+      return fail(TAQ_ERR_WORKSPACE_TOO_SMALL, "workspace: need %zu bytes, got %zu", need,
+                  ws_bytes);
+  }
   st = device_ok();
   if (st) return st;
   if (max_len == 0 || q_len == 0) return TAQ_OK;
@@ -351,6 +365,8 @@ taq_status prefill_common(const taq_kv_cache* k, const taq_kv_cache* v, const vo
   a.chunk = chunk ? 1 : 0;
   const int bq = 256 / a.r;
   a.n_qblk = (q_len + bq - 1) / bq;
+  a.nsplit = nsplit;
+  a.part = nsplit > 1 ? static_cast<float*>(ws) : nullptr;
   a.scale_log2 = scale_log2_of(softmax_scale, 128);
   hipError_t e = taq::launch_attn_prefill(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TAQ_OK : hip_fail(e, "attn_prefill launch");
@@ -365,15 +381,27 @@ taq_status taq_attn_prefill(const taq_kv_cache* k, const taq_kv_cache* v, const 
                             const taq_tile_mask* mask, float softmax_scale, void* o,
                             void* stream) {
   return prefill_common(k, v, q, hq, max_len, false, lens, max_len, mask, softmax_scale, o,
-                        stream);
+                        nullptr, 0, stream);
+}
+
+size_t taq_attn_prefill_chunk_workspace_bytes(const taq_kv_cache* k, int32_t hq, int32_t q_len,
+                                              int32_t max_len) {
+  if (!k || k->batch < 1 || k->num_kv_heads < 1 || hq < 1 || hq % k->num_kv_heads || q_len < 0 ||
+      max_len < 0)
+    return 0;
+  const int r = hq / k->num_kv_heads;
+  if (r != 1 && r != 2 && r != 4 && r != 8) return 0;
+  const int ns = taq::prefill_splits(k->batch, k->num_kv_heads, r, q_len, max_len);
+  return prefill_part_bytes(ns, k->batch, hq, q_len);
 }
 
 taq_status taq_attn_prefill_chunk(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
                                   int32_t hq, int32_t q_len, const int32_t* lens,
                                   int32_t max_len, const taq_tile_mask* mask,
-                                  float softmax_scale, void* o, void* stream) {
-  return prefill_common(k, v, q, hq, q_len, true, lens, max_len, mask, softmax_scale, o,
-                        stream);
+                                  float softmax_scale, void* o, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  return prefill_common(k, v, q, hq, q_len, true, lens, max_len, mask, softmax_scale, o, ws,
+                        ws_bytes, stream);
 }
 
 taq_status taq_kv_append(const taq_kv_cache* c, const void* x, const int32_t* starts,

@@ -39,6 +39,9 @@ constexpr int LDS_K = KT * KS_STRIDE;
 constexpr int LDS_V = D * VS_STRIDE;
 constexpr int LDS_STAGE = LDS_K + LDS_V;   // one tile (K-hat and V-hat^T)
 constexpr float NEG_BIG = -1.0e30f;
+// key-range partial of one (split, b, query head, row): m, l, 2 pad, acc[D]
+// (16-byte aligned records)
+constexpr int PART_REC = D + 4;
 #ifndef TAQ_PREFILL_READ_AHEAD
 #define TAQ_PREFILL_READ_AHEAD 3
 #endif
@@ -215,7 +218,8 @@ __device__ __forceinline__ bool mask_keep(const PrefillArgs& a, const uint8_t* m
 }
 
 template <int R, bool K8, bool V8>
-__device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n, char* lds) {
+__device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int split, int n,
+                             char* lds) {
   constexpr int BQ = 32 * (NWAVE / R);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -261,7 +265,12 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
   // rows of the workgroup that can see any key, and key range
   // last live position of the workgroup
   const int wg_last = min(min(q0 + BQ, a.Lq) - 1 + qoff, n - 1);
-  const int nkt = wg_last >= 0 ? wg_last / KT + 1 : 0;
+  const int nkt_all = wg_last >= 0 ? wg_last / KT + 1 : 0;
+  // key-range split: this workgroup takes tiles [kt_lo, nkt) of the query
+  // block's range (equal shares; the partials are merged afterwards)
+  const int per = (nkt_all + a.nsplit - 1) / a.nsplit;
+  const int kt_lo = min(split * per, nkt_all);
+  const int nkt = min(kt_lo + per, nkt_all);
   const int qt_first = max(q0 + qoff, 0) >> 7, qt_last = wg_last >= 0 ? (wg_last >> 7) : -1;
 
   auto wg_needs = [&](int kt) -> bool {
@@ -328,7 +337,7 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
   // dequantisation of tile j+2 into the third stage; tile j+3 is fetched from
   // HBM into registers.  Every wave walks the same tiles; rows a tile does not
   // reach are masked, so the loop has no per-wave branches.
-  const int t0_ = next_tile(0);
+  const int t0_ = next_tile(kt_lo);
   if (t0_ < nkt) {
     const int t1_ = next_tile(t0_ + 1);
     const int t2_ = t1_ < nkt ? next_tile(t1_ + 1) : nkt;
@@ -496,6 +505,25 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int n
 
   // ---- epilogue ----
   const float lt = l_run + lane_read_f(l_run, lane ^ 32);
+  if (a.nsplit > 1) {
+    // partial (max, normaliser, unnormalised accumulator) of this key range
+    if (row < a.Lq) {
+      float* dst = a.part + ((((int64_t)split * a.k.B + b) * a.Hq + hq) * a.Lq + row) * PART_REC;
+      if (hb == 0) {
+        dst[0] = m_run;
+        dst[1] = row_live ? lt : 0.f;
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq) {
+          const int d0 = 32 * db + 8 * vq + 4 * hb;
+          *reinterpret_cast<f32x4*>(dst + 4 + d0) =
+              f32x4{o[db][4 * vq], o[db][4 * vq + 1], o[db][4 * vq + 2], o[db][4 * vq + 3]};
+        }
+    }
+    return;
+  }
   const float inv = (row_live && lt > 0.f) ? 1.f / lt : 0.f;
   if (row < a.Lq) {
     uint16_t* op = a.o + (((int64_t)b * a.Hq + hq) * a.Lq + row) * D;
@@ -525,10 +553,38 @@ prefill_kernel(PrefillArgs a) {
   const int g = a.heads[id % H];
   const int rest = id / H;
   const int b = rest % B;
-  const int qblk = a.n_qblk - 1 - rest / B;
+  const int rest2 = rest / B;
+  const int split = rest2 % a.nsplit;
+  const int qblk = a.n_qblk - 1 - rest2 / a.nsplit;
   int n = a.lens[b];
   n = n < 0 ? 0 : (n > a.L ? a.L : n);
-  prefill_body<R, K8, V8>(a, b, g, qblk, n, lds);
+  prefill_body<R, K8, V8>(a, b, g, qblk, split, n, lds);
+}
+
+// Merge of the key-range partials: one wave per (b, query head, row), lane =
+// channel pair; splits are combined in split order.
+__global__ void __launch_bounds__(256)
+prefill_merge_kernel(PrefillArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rowid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (b, hq, row)
+  const int64_t nrow = (int64_t)a.k.B * a.Hq * a.Lq;
+  if (rowid >= nrow) return;
+  const int64_t sstride = nrow * PART_REC;
+  const float* src = a.part + rowid * PART_REC;
+  float M = NEG_BIG;
+  for (int sp = 0; sp < a.nsplit; ++sp) M = fmaxf(M, src[sp * sstride]);
+  float l = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int sp = 0; sp < a.nsplit; ++sp) {
+    const float* ps = src + sp * sstride;
+    const float f = fast_exp2(ps[0] - M);
+    l = fmaf(ps[1], f, l);
+    const float2 v = *reinterpret_cast<const float2*>(ps + 4 + 2 * lane);
+    o0 = fmaf(v.x, f, o0);
+    o1 = fmaf(v.y, f, o1);
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  half2v h = {(_Float16)(o0 * inv), (_Float16)(o1 * inv)};
+  *reinterpret_cast<half2v*>(a.o + rowid * D + 2 * lane) = h;
 }
 
 template <int R>
@@ -540,7 +596,7 @@ hipError_t launch_variants(PrefillArgs a, hipStream_t s) {
       if ((((a.k.is8 >> h) & 1ull) != 0) == k8 && (((a.v.is8 >> h) & 1ull) != 0) == v8)
         a.heads[a.nheads++] = (uint8_t)h;
     if (a.nheads == 0) continue;
-    const dim3 grid(a.n_qblk * a.nheads * a.k.B);
+    const dim3 grid(a.n_qblk * a.nsplit * a.nheads * a.k.B);
     switch (var) {
       case 0: hipLaunchKernelGGL((prefill_kernel<R, false, false>), grid, dim3(NT), 0, s, a); break;
       case 1: hipLaunchKernelGGL((prefill_kernel<R, false, true>), grid, dim3(NT), 0, s, a); break;
@@ -555,14 +611,32 @@ hipError_t launch_variants(PrefillArgs a, hipStream_t s) {
 
 }  // namespace
 
+int prefill_splits(int B, int Hkv, int r, int q_len, int max_len) {
+  // Enough workgroups to cover the CUs twice, each split keeping >= 4 key tiles.
+  const int bq = 32 * (NWAVE / r);
+  const int64_t wgs = (int64_t)B * Hkv * ((q_len + bq - 1) / bq);
+  const int tiles = (max_len + KT - 1) / KT;
+#ifndef TAQ_PREFILL_SPLIT_TARGET
+#define TAQ_PREFILL_SPLIT_TARGET 512
+#endif
+  int ns = 1;
+  while (ns < 16 && wgs * ns < TAQ_PREFILL_SPLIT_TARGET && tiles / (2 * ns) >= 4) ns *= 2;
+  return ns;
+}
+
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t s) {
+  hipError_t e;
   switch (a.r) {
-    case 1: return launch_variants<1>(a, s);
-    case 2: return launch_variants<2>(a, s);
-    case 4: return launch_variants<4>(a, s);
-    case 8: return launch_variants<8>(a, s);
+    case 1: e = launch_variants<1>(a, s); break;
+    case 2: e = launch_variants<2>(a, s); break;
+    case 4: e = launch_variants<4>(a, s); break;
+    case 8: e = launch_variants<8>(a, s); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess || a.nsplit <= 1) return e;
+  const int64_t nrow = (int64_t)a.k.B * a.Hq * a.Lq;
+  hipLaunchKernelGGL(prefill_merge_kernel, dim3((unsigned)((nrow + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace taq

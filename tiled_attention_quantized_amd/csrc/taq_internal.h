@@ -55,6 +55,8 @@ struct PrefillArgs {
   int32_t Lq;            // rows of q / o (L for a whole-sequence prefill)
   int32_t chunk;         // nonzero: row i sits at position n_b - Lq + i
   int32_t n_qblk;        // query blocks per (b, kv head) over Lq rows
+  int32_t nsplit;        // key-range splits per query block (1: write O directly)
+  float* part;           // nsplit > 1: partials [nsplit][B][Hq][Lq][D + 4] (m, l, -, -, acc)
   float scale_log2;
   int32_t nheads;        // KV heads handled by one launch, listed in heads[]
   uint8_t heads[TAQ_MAX_KV_HEADS];
@@ -80,6 +82,8 @@ hipError_t launch_head_assign(const uint16_t* o8, const uint16_t* o4, int B, int
 hipError_t launch_kv_dequantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t s, bool two_pass);
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t s);
+// Key-range splits the chunked prefill uses for these shapes (1 = none).
+int prefill_splits(int B, int Hkv, int r, int q_len, int max_len);
 
 // Decode split geometry chosen on the host (used for workspace sizing too).
 int decode_chunk_tokens(int B, int Hkv, int max_len);
