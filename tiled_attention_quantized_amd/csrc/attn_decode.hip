@@ -105,42 +105,85 @@ struct Ptrs {
   int cap;
 };
 
-// Loads of one 32-token step starting at t0 (a multiple of 32).  Offsets
-// inside one (batch, KV head) slab fit in 32 bits (at most capacity * 128
-// bytes), so every address is a uniform base plus a 32-bit lane offset.
+// Per-lane byte offsets of one step's loads, fixed for the whole loop: each
+// load is a wave-uniform base (moved by the step) plus one of these, so the
+// loop does no per-lane address arithmetic and every load destination keeps
+// its own registers while the next step's loads are in flight.
+struct LaneOffsets {
+  uint32_t k[2], kz[2], ks[2];   // per QK block bk
+  uint32_t v;                    // V codes (load db adds 16 db rows)
+  uint32_t vz, vs;               // V zeros / scales
+};
+
 template <bool K8, bool V8>
-__device__ __forceinline__ void load_step(const Ptrs& p, int t0, int i16, int lg, StepData& s) {
+__device__ __forceinline__ LaneOffsets lane_offsets(int i16, int lg, int cap) {
+  LaneOffsets o;
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk) {
-    const uint32_t T = (uint32_t)(t0 + qk_token<V8>(bk, i16));
-    if (K8) {
-      const u32x4* kp = reinterpret_cast<const u32x4*>(p.kbase + (T * D + 32 * lg));
-      s.kc[bk][0] = kp[0];
-      s.kc[bk][1] = kp[1];
-    } else {
-      s.kc[bk][0] = *reinterpret_cast<const u32x4*>(p.kbase + (T * (D / 2) + 16 * lg));
-    }
-    s.kz[bk] = p.kzero[T * 4 + lg];
-    s.ks[bk] = *reinterpret_cast<const u32x2*>(p.kscale + T * 4);
+    const uint32_t T = (uint32_t)qk_token<V8>(bk, i16);
+    o.k[bk] = K8 ? T * D + 32 * lg : T * (D / 2) + 16 * lg;
+    o.kz[bk] = T * 4 + lg;
+    o.ks[bk] = T * 8;                                      // 4 fp16 scales per token
+  }
+  o.v = (uint32_t)i16 * (V8 ? 32 : 16) + (V8 ? 8 : 4) * lg;
+  // lanes i16 = 0..3 of each row hold the row's tokens' scales and zeros of
+  // groups 0..3 (the other lanes repeat them); compute_step broadcasts them
+  o.vz = (uint32_t)(i16 & 3) * (uint32_t)cap + 8 * lg;
+  o.vs = 2 * o.vz;
+  return o;
+}
+
+// Buffer resources of one (batch, KV head) slab: a load is then a scalar
+// resource, a scalar offset that moves with the step and a fixed per-lane
+// offset, with no per-lane address arithmetic in the loop (and reads past a
+// slab's end return 0 instead of touching other memory).
+struct Rsrc {
+  __amdgpu_buffer_rsrc_t k, kz, ks, v, vz, vs;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+template <bool K8, bool V8>
+__device__ __forceinline__ Rsrc make_rsrcs(const Ptrs& p) {
+  Rsrc r;
+  const uint32_t cap = (uint32_t)p.cap;
+  r.k = make_rsrc(p.kbase, cap * (K8 ? D : D / 2));
+  r.kz = make_rsrc(p.kzero, cap * 4);
+  r.ks = make_rsrc(p.kscale, cap * 8);
+  r.v = make_rsrc(p.vbase, cap * (V8 ? D : D / 2));
+  r.vz = make_rsrc(p.vzero, cap * 4);
+  r.vs = make_rsrc(p.vscale, cap * 8);
+  return r;
+}
+
+// Loads of one 32-token step starting at t0 (a multiple of 32).
+template <bool K8, bool V8>
+__device__ __forceinline__ void load_step(const Rsrc& r, int t0, const LaneOffsets& o,
+                                          StepData& s) {
+  const int tk = t0 * (K8 ? D : D / 2);
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk) {
+    s.kc[bk][0] = __builtin_amdgcn_raw_buffer_load_b128(r.k, o.k[bk], tk, 0);
+    if (K8) s.kc[bk][1] = __builtin_amdgcn_raw_buffer_load_b128(r.k, o.k[bk] + 16, tk, 0);
+    s.kz[bk] = __builtin_amdgcn_raw_buffer_load_b8(r.kz, o.kz[bk], t0 * 4, 0);
+    s.ks[bk] = __builtin_amdgcn_raw_buffer_load_b64(r.ks, o.ks[bk], t0 * 8, 0);
   }
   // one V block of D channel rows per step; load db covers rows 16 db .. +15,
   // one contiguous 256 (int4) / 512 (int8) byte run per instruction
-  const uint8_t* vblk = p.vbase + (uint32_t)(t0 >> 5) * (uint32_t)(D * (V8 ? 32 : 16));
+  const int tv = (t0 >> 5) * (D * (V8 ? 32 : 16));
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
-    const uint32_t d = 16 * db + i16;
     if (V8) {
-      s.vc[db] = *reinterpret_cast<const u32x2*>(vblk + (d * 32 + 8 * lg));
+      s.vc[db] = __builtin_amdgcn_raw_buffer_load_b64(r.v, o.v + 512 * db, tv, 0);
     } else {
-      s.vc[db][0] = *reinterpret_cast<const uint32_t*>(vblk + (d * 16 + 4 * lg));
+      s.vc[db][0] = __builtin_amdgcn_raw_buffer_load_b32(r.v, o.v + 256 * db, tv, 0);
       s.vc[db][1] = 0u;
     }
   }
-  // lanes i16 = 0..3 of each row hold the row's tokens' scales and zeros of
-  // groups 0..3 (the other lanes repeat them); compute_step broadcasts them
-  const uint32_t mo = (uint32_t)(i16 & 3) * (uint32_t)p.cap + (uint32_t)(t0 + 8 * lg);
-  s.vz = *reinterpret_cast<const u32x2*>(p.vzero + mo);
-  s.vs = *reinterpret_cast<const u32x4*>(p.vscale + mo);
+  s.vz = __builtin_amdgcn_raw_buffer_load_b64(r.vz, o.vz, t0, 0);
+  s.vs = __builtin_amdgcn_raw_buffer_load_b128(r.vs, o.vs, 2 * t0, 0);
 }
 
 template <int R, bool K8, bool V8>
@@ -410,9 +453,15 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
     tbits = 0;
     for (int k = 0; k <= tile1 - tile0; ++k) tbits |= (mrow[tile0 + k] ? 1u : 0u) << k;
   }
+  // first step at or after t whose tile is kept (t_end if none): a find-first-
+  // set on the wave-uniform keep bits, no loop
   auto next_step = [&](int t) -> int {
-    while (t < t_end && !((tbits >> ((t >> 7) - tile0)) & 1u)) t += STEP;
-    return t;
+    if (t >= t_end) return t;
+    const int k = (t >> 7) - tile0;
+    const uint32_t rest = tbits >> k;
+    if (rest & 1u) return t;
+    if (rest == 0u) return t_end;
+    return (tile0 + k + __builtin_ctz(rest)) << 7;
   };
 
   // ---- two-buffer pipeline over the wave's steps -----------------------------
@@ -420,25 +469,29 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
   // computed.  Every iteration issues exactly one step of loads (past the end:
   // a repeat of a valid step that is never used), so the number of loads in
   // flight is the same on every path and each wait before a use is partial.
-  // (A third buffer for the int4 variant measured no faster.)
-  auto addr = [&](int t) { return t < t_end ? t : t_safe; };
+  // (A third buffer measured no faster: the loop is bound by its compute.)
+  // Step starts are wave-uniform: keep them scalar (they are the scalar
+  // offsets of the buffer loads).
+  auto addr = [&](int t) { return __builtin_amdgcn_readfirstlane(t < t_end ? t : t_safe); };
+  const LaneOffsets lo = lane_offsets<K8, V8>(i16, lg, p.cap);
+  const Rsrc rs = make_rsrcs<K8, V8>(p);
   StepData A, Bf;
   int t_cur = next_step(t_begin);
   if (t_cur < t_end) {
-    load_step<K8, V8>(p, t_cur, i16, lg, A);
+    load_step<K8, V8>(rs, addr(t_cur), lo, A);
     int t_nxt = next_step(t_cur + STEP);
-    load_step<K8, V8>(p, addr(t_nxt), i16, lg, Bf);
+    load_step<K8, V8>(rs, addr(t_nxt), lo, Bf);
     while (true) {
       compute_step<R, K8, V8, MODE>(a, ws, A, t_end - t_cur, i16, lg);
       t_cur = t_nxt;
       if (t_cur >= t_end) break;
       t_nxt = next_step(t_cur + STEP);
-      load_step<K8, V8>(p, addr(t_nxt), i16, lg, A);
+      load_step<K8, V8>(rs, addr(t_nxt), lo, A);
       compute_step<R, K8, V8, MODE>(a, ws, Bf, t_end - t_cur, i16, lg);
       t_cur = t_nxt;
       if (t_cur >= t_end) break;
       t_nxt = next_step(t_cur + STEP);
-      load_step<K8, V8>(p, addr(t_nxt), i16, lg, Bf);
+      load_step<K8, V8>(rs, addr(t_nxt), lo, Bf);
     }
   }
 
