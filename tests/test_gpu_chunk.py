@@ -189,3 +189,18 @@ def test_chunk_key_range_split(r):
     assert max_abs(got, want) <= TOL
     assert max_abs(got, one) <= TOL
     assert not got[2, :, :Lq - 60].any()          # rows at negative positions
+
+
+@pytest.mark.parametrize("bits,n8", [(4, 0), (4, 1)])
+def test_chunk_key_range_split_int4_and_mixed(bits, n8):
+    """The split path over int4 and mixed int4/int8 heads (r = 2), with a
+    one-row chunk and a chunk longer than one query block."""
+    require_gpu()
+    cap = 4096
+    lens = np.array([4096, 3000, 77], dtype=np.int32)
+    for Lq in (1, 300):
+        note(f"chunk split bits={bits} n8={n8} Lq={Lq}")
+        (got, one), want = _chunk_case(2, Lq, lens, cap, seed=520 + Lq + n8, bits=bits,
+                                       n_int8=n8, also_unsplit=True)
+        assert max_abs(got, want) <= TOL
+        assert max_abs(got, one) <= TOL
