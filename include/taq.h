@@ -27,7 +27,8 @@
  * Memory layout (all buffers contiguous, owned by the caller)
  * -------------------------------------------------------------
  * A cache (K or V) has batch B, num_kv_heads Hkv, head_dim D (= 128 for the
- * attention calls; any multiple of 32 for quantise/dequantise), capacity C
+ * attention calls; any multiple of 32 up to 1024 for quantise/dequantise),
+ * capacity C
  * (a multiple of 128) and per-head bit widths bits[h] in {4, 8}.
  * RB(h) = D * bits[h] / 8 code bytes per token.  The codes of (b, h) start at
  *     b * C * sum_h RB(h)  +  C * sum_{h' < h} RB(h').
@@ -54,8 +55,10 @@
  *   is not gfx950 gets TAQ_ERR_UNSUPPORTED.
  * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *   default stream).  Buffers must stay alive until the stream reaches it.
- * - The library allocates no device memory; decode scratch is the caller's
- *   `workspace`, sized by taq_attn_decode_workspace_bytes.
+ * - The library allocates no device memory; scratch data goes to caller
+ *   workspaces, each sized by its *_workspace_bytes call (decode partials,
+ *   chunked-prefill key-range partials, mask-generator sums and scores,
+ *   head-sensitivity caches).
  * - Device pointers must be 16-byte aligned (TAQ_ERR_MISALIGNED otherwise).
  * - Device-resident lengths are clamped to [0, max_seq_len] by the kernels.
  * - softmax_scale = 0 means 1/sqrt(head_dim); negative scales are UNSUPPORTED.
