@@ -28,7 +28,7 @@
  * -------------------------------------------------------------
  * A cache (K or V) has batch B, num_kv_heads Hkv, head_dim D (= 128 for the
  * attention calls; any multiple of 32 up to 1024 for quantise/dequantise),
- * capacity C
+ * capacity C (attention calls: C * D < 2^31)
  * (a multiple of 128) and per-head bit widths bits[h] in {4, 8}.
  * RB(h) = D * bits[h] / 8 code bytes per token.  The codes of (b, h) start at
  *     b * C * sum_h RB(h)  +  C * sum_{h' < h} RB(h').

@@ -131,6 +131,8 @@ def test_attention_rejects(call):
     assert call(k=k64)[0] == UNSUPPORTED                 # attention needs D = 128
     v2 = cache(B=1, H=2, cap=384, bits=(8, 8), layout=1)
     assert call(v=v2)[0] == INVALID                      # geometry mismatch
+    kbig = cache(B=1, H=2, cap=1 << 24, bits=(8, 8), layout=0)
+    assert call(k=kbig, max_len=200)[0] == UNSUPPORTED   # slab offsets beyond 32 bits
     bad_tile = T._Mask(FAKE, 64, 2, 2, 0, 0)
     assert call(mask=bad_tile)[0] == UNSUPPORTED
     small = T._Mask(FAKE, 128, 2, 1, 0, 0)

@@ -48,6 +48,10 @@ taq_status check_cache(const taq_kv_cache* c, const char* name, int need_layout,
                 name);
   if (attention && c->head_dim != 128)
     return fail(TAQ_ERR_UNSUPPORTED, "%s: attention kernels need head_dim 128", name);
+  // the attention kernels address one (batch, head) slab with 32-bit offsets
+  if (attention && (int64_t)c->capacity * c->head_dim >= ((int64_t)1 << 31))
+    return fail(TAQ_ERR_UNSUPPORTED, "%s: capacity %d too large for the attention kernels "
+                "(capacity * head_dim must stay below 2^31)", name, c->capacity);
   if (c->capacity <= 0 || c->capacity % TAQ_TILE)
     return fail(TAQ_ERR_INVALID_ARGUMENT, "%s: capacity must be a positive multiple of 128",
                 name);
