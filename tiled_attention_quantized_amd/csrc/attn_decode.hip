@@ -90,7 +90,9 @@ struct StepData {
   u32x4 kc[2][2];   // K codes of the lane's two tokens (group lg); int4 uses [bk][0]
   uint32_t kz[2];   // K zero bytes of those tokens (group lg)
   u32x2 ks[2];      // K scales of those tokens (all 4 groups)
-  u32x2 vc[8];      // V codes: channel 16*db + i16, tokens 8*lg .. +7 (int4: vc[db][0])
+  u32x2 vc[8];      // V codes: channel 16*db + i16, tokens 8*lg .. +7 (int8 only)
+  u32x4 vw[2];      // int4: the step's 2 KB V block, row L (16 bytes) in lane L of vw[0]
+                    // (rows 0..63) and of vw[1] (rows 64..127)
   u32x2 vz;         // V zeros of the lane's 8 tokens (group i16 % 4)
   u32x4 vs;         // V scales of the lane's 8 tokens (group i16 % 4)
 };
@@ -113,6 +115,7 @@ struct LaneOffsets {
   uint32_t k[2], kz[2], ks[2];   // per QK block bk
   uint32_t v;                    // V codes (load db adds 16 db rows)
   uint32_t vz, vs;               // V zeros / scales
+  uint32_t vrow;                 // int4: the lane's 16-byte row of the V block
 };
 
 template <bool K8, bool V8>
@@ -130,6 +133,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int i16, int lg, int cap) {
   // groups 0..3 (the other lanes repeat them); compute_step broadcasts them
   o.vz = (uint32_t)(i16 & 3) * (uint32_t)cap + 8 * lg;
   o.vs = 2 * o.vz;
+  o.vrow = 16u * (uint32_t)(16 * lg + i16);
   return o;
 }
 
@@ -173,14 +177,16 @@ __device__ __forceinline__ void load_step(const Rsrc& r, int t0, const LaneOffse
   // one V block of D channel rows per step; load db covers rows 16 db .. +15,
   // one contiguous 256 (int4) / 512 (int8) byte run per instruction
   const int tv = (t0 >> 5) * (D * (V8 ? 32 : 16));
+  if (V8) {
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
-    if (V8) {
+    for (int db = 0; db < 8; ++db)
       s.vc[db] = __builtin_amdgcn_raw_buffer_load_b64(r.v, o.v + 512 * db, tv, 0);
-    } else {
-      s.vc[db][0] = __builtin_amdgcn_raw_buffer_load_b32(r.v, o.v + 256 * db, tv, 0);
-      s.vc[db][1] = 0u;
-    }
+  } else {
+    // two 16-byte loads per lane instead of eight 4-byte ones (the memory
+    // pipeline's instruction rate, not its bandwidth, limited the step);
+    // compute_step redistributes the rows through LDS
+    s.vw[0] = __builtin_amdgcn_raw_buffer_load_b128(r.v, o.vrow, tv, 0);
+    s.vw[1] = __builtin_amdgcn_raw_buffer_load_b128(r.v, o.vrow + 1024, tv, 0);
   }
   s.vz = __builtin_amdgcn_raw_buffer_load_b64(r.vz, o.vz, t0, 0);
   s.vs = __builtin_amdgcn_raw_buffer_load_b128(r.vs, o.vs, 2 * t0, 0);
@@ -203,7 +209,8 @@ __device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
 // PV for the two V loads of quantisation group GQ: that group's scales and
 // zero-points of the row's 8 tokens come from lane GQ of the row.
 template <bool V8, int GQ>
-__device__ __forceinline__ void pv_group(f32x4 (&acc)[8], const StepData& s, half8 bp,
+__device__ __forceinline__ void pv_group(f32x4 (&acc)[8], const StepData& s,
+                                         const u32x2 (&vc)[8], half8 bp,
                                          const uint32_t (&keep)[4]) {
   u32x2 z;
   u32x4 sc;
@@ -222,7 +229,7 @@ __device__ __forceinline__ void pv_group(f32x4 (&acc)[8], const StepData& s, hal
     u32x4 o;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const half2v cz = u32_to_h2(v_code_pair<V8>(s.vc[db], m)) + u32_to_h2(nzp[m]);
+      const half2v cz = u32_to_h2(v_code_pair<V8>(vc[db], m)) + u32_to_h2(nzp[m]);
       o[m] = h2_to_u32(cz * u32_to_h2(scp[m]));
     }
     acc[db] = mfma16x16x32(u4_to_h8(o), bp, acc[db]);
@@ -231,7 +238,8 @@ __device__ __forceinline__ void pv_group(f32x4 (&acc)[8], const StepData& s, hal
 
 template <int R, bool K8, bool V8, int MODE>
 __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K8, V8>& ws,
-                                             StepData& s, int nvalid, int i16, int lg) {
+                                             StepData& s, int nvalid, int i16, int lg,
+                                             uint32_t* vst) {
   constexpr int NRB = WaveState<R, K8, V8>::NRB;
   // ---------------- scores ----------------
   float sc[NRB][2];
@@ -360,20 +368,40 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
     keep[j] = (ta < nvalid ? 0x0000FFFFu : 0u) | (ta + 1 < nvalid ? 0xFFFF0000u : 0u);
   }
   // loads 2 gq and 2 gq + 1 are channels of group gq
-  pv_group<V8, 0>(ws.acc, s, bp, keep);
-  pv_group<V8, 1>(ws.acc, s, bp, keep);
-  pv_group<V8, 2>(ws.acc, s, bp, keep);
-  pv_group<V8, 3>(ws.acc, s, bp, keep);
+  // V codes in the operand layout: lane (i16, lg) takes row 16 db + i16,
+  // tokens 8 lg .. +7.  int4 rows arrive one per lane and go through the
+  // wave's own 2 KB of LDS (LDS operations of one wave run in order, so no
+  // barrier; the reads are conflict-free: 64 consecutive dwords per read).
+  u32x2 vc[8];
+  if constexpr (V8) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) vc[db] = s.vc[db];
+  } else {
+    const int lane = 16 * lg + i16;
+    *reinterpret_cast<u32x4*>(vst + 4 * lane) = s.vw[0];
+    *reinterpret_cast<u32x4*>(vst + 256 + 4 * lane) = s.vw[1];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      vc[db][0] = vst[4 * (16 * db + i16) + lg];
+      vc[db][1] = 0u;
+    }
+  }
+  pv_group<V8, 0>(ws.acc, s, vc, bp, keep);
+  pv_group<V8, 1>(ws.acc, s, vc, bp, keep);
+  pv_group<V8, 2>(ws.acc, s, vc, bp, keep);
+  pv_group<V8, 3>(ws.acc, s, vc, bp, keep);
 }
 
 template <int R, bool K8, bool V8, int MODE>
-__device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, float* lds) {
+__device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, float* lds,
+                            uint32_t* vstage) {
   constexpr int NRB = (R + 3) / 4;
   const int lane = threadIdx.x & 63;
   // wave index as a scalar: all token-range and loop control below is
   // wave-uniform, so it runs on the scalar unit with real branches
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15;
+  uint32_t* vst = V8 ? vstage : vstage + w * 512;   // the wave's int4 V staging
   const int lg = lane >> 4;
 
   const CacheGeom& K = a.k;
@@ -482,12 +510,12 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
     int t_nxt = next_step(t_cur + STEP);
     load_step<K8, V8>(rs, addr(t_nxt), lo, Bf);
     while (true) {
-      compute_step<R, K8, V8, MODE>(a, ws, A, t_end - t_cur, i16, lg);
+      compute_step<R, K8, V8, MODE>(a, ws, A, t_end - t_cur, i16, lg, vst);
       t_cur = t_nxt;
       if (t_cur >= t_end) break;
       t_nxt = next_step(t_cur + STEP);
       load_step<K8, V8>(rs, addr(t_nxt), lo, A);
-      compute_step<R, K8, V8, MODE>(a, ws, Bf, t_end - t_cur, i16, lg);
+      compute_step<R, K8, V8, MODE>(a, ws, Bf, t_end - t_cur, i16, lg, vst);
       t_cur = t_nxt;
       if (t_cur >= t_end) break;
       t_nxt = next_step(t_cur + STEP);
@@ -563,6 +591,7 @@ template <int R, bool K8, bool V8, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_split_kernel(DecodeArgs a) {
   __shared__ float lds[2 * WAVES * R + WAVES * R * D];
+  __shared__ __attribute__((aligned(16))) uint32_t vstage[V8 ? 1 : WAVES * 512];
   const int units = a.k.B * a.nheads;
 #ifdef TAQ_DECODE_CHUNK_FASTEST
   const int u = blockIdx.x / a.nchunk;
@@ -576,7 +605,7 @@ decode_split_kernel(DecodeArgs a) {
   int n = a.lens[b];
   n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
   if (c * a.chunk >= n) return;
-  decode_body<R, K8, V8, MODE>(a, b, g, c, n, lds);
+  decode_body<R, K8, V8, MODE>(a, b, g, c, n, lds, vstage);
 }
 
 // One workgroup per (batch, query head).  Every wave finds the global maximum
