@@ -90,9 +90,8 @@ struct StepData {
   u32x4 kc[2][2];   // K codes of the lane's two tokens (group lg); int4 uses [bk][0]
   uint32_t kz[2];   // K zero bytes of those tokens (group lg)
   u32x2 ks[2];      // K scales of those tokens (all 4 groups)
-  u32x2 vc[8];      // V codes: channel 16*db + i16, tokens 8*lg .. +7 (int8 only)
-  u32x4 vw[2];      // int4: the step's 2 KB V block, row L (16 bytes) in lane L of vw[0]
-                    // (rows 0..63) and of vw[1] (rows 64..127)
+  u32x4 vw[4];      // the step's V block, 16 bytes per lane per load: load k holds bytes
+                    // 1024 k + 16 L .. +15 in lane L (int8: 4 KB, four loads; int4: 2 KB, two)
   u32x2 vz;         // V zeros of the lane's 8 tokens (group i16 % 4)
   u32x4 vs;         // V scales of the lane's 8 tokens (group i16 % 4)
 };
@@ -113,9 +112,8 @@ struct Ptrs {
 // its own registers while the next step's loads are in flight.
 struct LaneOffsets {
   uint32_t k[2], kz[2], ks[2];   // per QK block bk
-  uint32_t v;                    // V codes (load db adds 16 db rows)
   uint32_t vz, vs;               // V zeros / scales
-  uint32_t vrow;                 // int4: the lane's 16-byte row of the V block
+  uint32_t vrow;                 // V codes: the lane's 16 bytes of each 1 KB of the block
 };
 
 template <bool K8, bool V8>
@@ -128,7 +126,6 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int i16, int lg, int cap) {
     o.kz[bk] = T * 4 + lg;
     o.ks[bk] = T * 8;                                      // 4 fp16 scales per token
   }
-  o.v = (uint32_t)i16 * (V8 ? 32 : 16) + (V8 ? 8 : 4) * lg;
   // lanes i16 = 0..3 of each row hold the row's tokens' scales and zeros of
   // groups 0..3 (the other lanes repeat them); compute_step broadcasts them
   o.vz = (uint32_t)(i16 & 3) * (uint32_t)cap + 8 * lg;
@@ -177,17 +174,12 @@ __device__ __forceinline__ void load_step(const Rsrc& r, int t0, const LaneOffse
   // one V block of D channel rows per step; load db covers rows 16 db .. +15,
   // one contiguous 256 (int4) / 512 (int8) byte run per instruction
   const int tv = (t0 >> 5) * (D * (V8 ? 32 : 16));
-  if (V8) {
+  // 16-byte loads over the contiguous block (the memory pipeline's
+  // instruction rate, not its bandwidth, limited the step with one 4- or
+  // 8-byte operand piece per load); compute_step redistributes through LDS
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-      s.vc[db] = __builtin_amdgcn_raw_buffer_load_b64(r.v, o.v + 512 * db, tv, 0);
-  } else {
-    // two 16-byte loads per lane instead of eight 4-byte ones (the memory
-    // pipeline's instruction rate, not its bandwidth, limited the step);
-    // compute_step redistributes the rows through LDS
-    s.vw[0] = __builtin_amdgcn_raw_buffer_load_b128(r.v, o.vrow, tv, 0);
-    s.vw[1] = __builtin_amdgcn_raw_buffer_load_b128(r.v, o.vrow + 1024, tv, 0);
-  }
+  for (int k = 0; k < (V8 ? 4 : 2); ++k)
+    s.vw[k] = __builtin_amdgcn_raw_buffer_load_b128(r.v, o.vrow + 1024 * k, tv, 0);
   s.vz = __builtin_amdgcn_raw_buffer_load_b64(r.vz, o.vz, t0, 0);
   s.vs = __builtin_amdgcn_raw_buffer_load_b128(r.vs, o.vs, 2 * t0, 0);
 }
@@ -369,19 +361,19 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
   }
   // loads 2 gq and 2 gq + 1 are channels of group gq
   // V codes in the operand layout: lane (i16, lg) takes row 16 db + i16,
-  // tokens 8 lg .. +7.  int4 rows arrive one per lane and go through the
-  // wave's own 2 KB of LDS (LDS operations of one wave run in order, so no
-  // barrier; the reads are conflict-free: 64 consecutive dwords per read).
+  // tokens 8 lg .. +7.  The block goes through the wave's own LDS (LDS
+  // operations of one wave run in order, so no barrier; every read is one
+  // contiguous run over the 64 lanes, free of bank conflicts).
+  const int lane = 16 * lg + i16;
+#pragma unroll
+  for (int k = 0; k < (V8 ? 4 : 2); ++k)
+    *reinterpret_cast<u32x4*>(vst + 256 * k + 4 * lane) = s.vw[k];
   u32x2 vc[8];
-  if constexpr (V8) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db) vc[db] = s.vc[db];
-  } else {
-    const int lane = 16 * lg + i16;
-    *reinterpret_cast<u32x4*>(vst + 4 * lane) = s.vw[0];
-    *reinterpret_cast<u32x4*>(vst + 256 + 4 * lane) = s.vw[1];
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
+  for (int db = 0; db < 8; ++db) {
+    if constexpr (V8) {
+      vc[db] = *reinterpret_cast<const u32x2*>(vst + 8 * (16 * db + i16) + 2 * lg);
+    } else {
       vc[db][0] = vst[4 * (16 * db + i16) + lg];
       vc[db][1] = 0u;
     }
@@ -401,7 +393,7 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
   // wave-uniform, so it runs on the scalar unit with real branches
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15;
-  uint32_t* vst = V8 ? vstage : vstage + w * 512;   // the wave's int4 V staging
+  uint32_t* vst = vstage + w * (V8 ? 1024 : 512);   // the wave's V staging
   const int lg = lane >> 4;
 
   const CacheGeom& K = a.k;
@@ -591,7 +583,7 @@ template <int R, bool K8, bool V8, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_split_kernel(DecodeArgs a) {
   __shared__ float lds[2 * WAVES * R + WAVES * R * D];
-  __shared__ __attribute__((aligned(16))) uint32_t vstage[V8 ? 1 : WAVES * 512];
+  __shared__ __attribute__((aligned(16))) uint32_t vstage[WAVES * (V8 ? 1024 : 512)];
   const int units = a.k.B * a.nheads;
 #ifdef TAQ_DECODE_CHUNK_FASTEST
   const int u = blockIdx.x / a.nchunk;
