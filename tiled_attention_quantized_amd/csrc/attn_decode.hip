@@ -195,26 +195,23 @@ struct WaveState {
 // Lane N of each 16-lane row copied to the whole row (DPP row_newbcast).
 template <int N>
 __device__ __forceinline__ uint32_t row_bcast(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x150 + N, 0xF, 0xF, false);
+  // every lane of a row reads a live lane, so no "old" value (and no
+  // register initialisation) is needed
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x150 + N, 0xF, 0xF, true);
 }
 
-// PV for the two V loads of quantisation group GQ: that group's scales and
-// zero-points of the row's 8 tokens come from lane GQ of the row.
+// PV for the two V loads of quantisation group GQ.  Every lane prepares the
+// operand pairs (negated biased zero-points, masked scales) of its own group
+// for the row's 8 tokens (nzl, scl); group GQ's come from lane GQ of the row.
 template <bool V8, int GQ>
-__device__ __forceinline__ void pv_group(f32x4 (&acc)[8], const StepData& s,
-                                         const u32x2 (&vc)[8], half8 bp,
-                                         const uint32_t (&keep)[4]) {
-  u32x2 z;
-  u32x4 sc;
-  z[0] = row_bcast<GQ>(s.vz[0]);
-  z[1] = row_bcast<GQ>(s.vz[1]);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) sc[j] = row_bcast<GQ>(s.vs[j]) & keep[j];
+__device__ __forceinline__ void pv_group(f32x4 (&acc)[8], const u32x2 (&vc)[8],
+                                         const uint32_t (&nzl)[4], const uint32_t (&scl)[4],
+                                         half8 bp) {
   uint32_t nzp[4], scp[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    nzp[m] = v_negz_pair<V8>(z, m);
-    scp[m] = v_scale_pair<V8>(sc, m);
+    nzp[m] = row_bcast<GQ>(nzl[m]);
+    scp[m] = row_bcast<GQ>(scl[m]);
   }
 #pragma unroll
   for (int db = 2 * GQ; db < 2 * GQ + 2; ++db) {
@@ -378,10 +375,23 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
       vc[db][1] = 0u;
     }
   }
-  pv_group<V8, 0>(ws.acc, s, vc, bp, keep);
-  pv_group<V8, 1>(ws.acc, s, vc, bp, keep);
-  pv_group<V8, 2>(ws.acc, s, vc, bp, keep);
-  pv_group<V8, 3>(ws.acc, s, vc, bp, keep);
+  // the lane's own group: zero-point and (tail-masked) scale pairs, once per
+  // step rather than once per broadcast
+  uint32_t nzl[4], scl[4];
+  {
+    u32x4 svm;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) svm[j] = s.vs[j] & keep[j];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      nzl[m] = v_negz_pair<V8>(s.vz, m);
+      scl[m] = v_scale_pair<V8>(svm, m);
+    }
+  }
+  pv_group<V8, 0>(ws.acc, vc, nzl, scl, bp);
+  pv_group<V8, 1>(ws.acc, vc, nzl, scl, bp);
+  pv_group<V8, 2>(ws.acc, vc, nzl, scl, bp);
+  pv_group<V8, 3>(ws.acc, vc, nzl, scl, bp);
 }
 
 template <int R, bool K8, bool V8, int MODE>
