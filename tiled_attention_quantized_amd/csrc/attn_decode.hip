@@ -68,8 +68,11 @@ __device__ __forceinline__ uint32_t v_negz_pair(u32x2 z8, int m) {
     const uint32_t w = m < 2 ? z8[0] : z8[1];
     return perm_b32(vconst(0xE4E4E4E4u), w, (m & 1) ? 0x04030402u : 0x04010400u);
   }
+  // int4: the code pair m comes from nibbles_to_biased_h2(., ., m), whose
+  // bias is 1024 for even m and 64 for odd m
   const uint32_t sel = (uint32_t)m | (0x0Cu << 8) | ((uint32_t)(4 + m) << 16) | (0x0Cu << 24);
-  return perm_b32(z8[1], z8[0], sel) | 0xE400E400u;
+  const uint32_t nz = perm_b32(z8[1], z8[0], sel) | 0xE400E400u;
+  return (m & 1) ? odd_nibble_negz(nz) : nz;
 }
 
 template <bool V8>
@@ -80,9 +83,9 @@ __device__ __forceinline__ uint32_t v_scale_pair(u32x4 s8, int m) {
 }
 
 template <bool V8>
-__device__ __forceinline__ uint32_t v_code_pair(u32x2 c8, int m) {
+__device__ __forceinline__ uint32_t v_code_pair(u32x2 c8, uint32_t c8s, int m) {
   if (V8) return bytes_to_biased_h2(m < 2 ? c8[0] : c8[1], m & 1);
-  return nibbles_to_biased_h2(c8[0], m);
+  return nibbles_to_biased_h2(c8[0], c8s, m);
 }
 
 // Raw bytes of one 32-token step held by one lane.
@@ -216,9 +219,10 @@ __device__ __forceinline__ void pv_group(f32x4 (&acc)[8], const u32x2 (&vc)[8],
 #pragma unroll
   for (int db = 2 * GQ; db < 2 * GQ + 2; ++db) {
     u32x4 o;
+    const uint32_t c8s = V8 ? 0u : vc[db][0] >> 8;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const half2v cz = u32_to_h2(v_code_pair<V8>(vc[db], m)) + u32_to_h2(nzp[m]);
+      const half2v cz = u32_to_h2(v_code_pair<V8>(vc[db], c8s, m)) + u32_to_h2(nzp[m]);
       o[m] = h2_to_u32(cz * u32_to_h2(scp[m]));
     }
     acc[db] = mfma16x16x32(u4_to_h8(o), bp, acc[db]);
@@ -252,13 +256,15 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
       }
     } else {
       const u32x4 cw = s.kc[bk][0];
+      const uint32_t nzo = odd_nibble_negz(nz);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         u32x4 o;
+        const uint32_t cws = cw[kk] >> 8;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint32_t h2 = nibbles_to_biased_h2(cw[kk], k);
-          o[k] = h2_to_u32(u32_to_h2(h2) + u32_to_h2(nz));
+          const uint32_t h2 = nibbles_to_biased_h2(cw[kk], cws, k);
+          o[k] = h2_to_u32(u32_to_h2(h2) + u32_to_h2((k & 1) ? nzo : nz));
         }
         bk8[kk] = u4_to_h8(o);
       }
@@ -266,7 +272,6 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
     const u32x2 sraw = s.ks[bk];
     const float s0 = (float)u32_to_h2(sraw[0])[0], s1 = (float)u32_to_h2(sraw[0])[1];
     const float s2 = (float)u32_to_h2(sraw[1])[0], s3 = (float)u32_to_h2(sraw[1])[1];
-    const bool valid = tl < nvalid;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
@@ -278,7 +283,24 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
       x = fmaf(s3, d4[3], x);
       x *= a.scale_log2;
       const bool live = 4 * rb + lg < R;
-      sc[rb][bk] = valid ? (live ? x : 0.f) : -INFINITY;
+      sc[rb][bk] = live ? x : 0.f;
+    }
+  }
+  // The chunk's last step may hold fewer than STEP tokens (wave-uniform and
+  // rare, so a real branch rather than selects on every step): tokens past
+  // the end get score -inf and a zero V scale, so their weight and their
+  // V-hat are exactly 0 whatever the cache holds there.
+  if (nvalid < STEP) {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+      if (qk_token<V8>(bk, i16) >= nvalid)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) sc[rb][bk] = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ta = 8 * lg + 2 * j;
+      s.vs[j] &= (ta < nvalid ? 0x0000FFFFu : 0u) | (ta + 1 < nvalid ? 0xFFFF0000u : 0u);
     }
   }
 
@@ -331,7 +353,9 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
       const uint32_t v1 = lane_read(p2[NRB - 1], src);
       v = (hcol >> 2) ? v1 : v;
     }
-    pb[mm] = hcol < R ? v : 0u;
+    // columns hcol >= R repeat a finite row of another column; their
+    // accumulator columns are never written out
+    pb[mm] = v;
   }
   if (rescale) {
     // rare: keep it a real branch (an empty volatile asm stops the compiler
@@ -348,14 +372,6 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
   const half8 bp = u4_to_h8(pb);
 
   // ---------------- V-hat^T operand and PV ----------------
-  // zero the scales of tokens past the end so their V-hat is exactly 0
-  // (branch-free selects: no divergent control flow inside the step)
-  uint32_t keep[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ta = 8 * lg + 2 * j;
-    keep[j] = (ta < nvalid ? 0x0000FFFFu : 0u) | (ta + 1 < nvalid ? 0xFFFF0000u : 0u);
-  }
   // loads 2 gq and 2 gq + 1 are channels of group gq
   // V codes in the operand layout: lane (i16, lg) takes row 16 db + i16,
   // tokens 8 lg .. +7.  The block goes through the wave's own LDS (LDS
@@ -378,15 +394,10 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
   // the lane's own group: zero-point and (tail-masked) scale pairs, once per
   // step rather than once per broadcast
   uint32_t nzl[4], scl[4];
-  {
-    u32x4 svm;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) svm[j] = s.vs[j] & keep[j];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      nzl[m] = v_negz_pair<V8>(s.vz, m);
-      scl[m] = v_scale_pair<V8>(svm, m);
-    }
+  for (int m = 0; m < 4; ++m) {
+    nzl[m] = v_negz_pair<V8>(s.vz, m);
+    scl[m] = v_scale_pair<V8>(s.vs, m);
   }
   pv_group<V8, 0>(ws.acc, vc, nzl, scl, bp);
   pv_group<V8, 1>(ws.acc, vc, nzl, scl, bp);

@@ -53,9 +53,19 @@ __device__ __forceinline__ uint32_t bytes_to_biased_h2(uint32_t w, bool hi_pair)
   return perm_b32(vconst(0x64646464u), w, hi_pair ? 0x04030402u : 0x04010400u);
 }
 
-// Two nibbles at bit offsets 4k and 16 + 4k of w -> half2 (1024 + n, 1024 + n').
-__device__ __forceinline__ uint32_t nibbles_to_biased_h2(uint32_t w, int k) {
-  return and_or(k ? (w >> (4 * k)) : w, 0x000F000Fu, 0x64006400u);
+// Two nibbles at bit offsets 4k and 16 + 4k of w -> half2 of biased values,
+// exact: even k gives (1024 + n, 1024 + n'), the nibbles landing in mantissa
+// bits 0..3 of 1024; odd k gives (64 + n, 64 + n'), the nibbles landing in
+// mantissa bits 4..7 of 64 (whose unit in the last place is 1/16), so no
+// shift is needed for k = 1 and one shared shift (w8 = w >> 8) serves k = 2, 3.
+__device__ __forceinline__ uint32_t nibbles_to_biased_h2(uint32_t w, uint32_t w8, int k) {
+  const uint32_t x = k < 2 ? w : w8;
+  return (k & 1) ? and_or(x, 0x00F000F0u, 0x54005400u) : and_or(x, 0x000F000Fu, 0x64006400u);
+}
+// The bias of nibbles_to_biased_h2's odd pairs is 960 below that of its even
+// pairs: -(1024 + z) half2 -> -(64 + z) half2, exact for every zero byte z.
+__device__ __forceinline__ uint32_t odd_nibble_negz(uint32_t nz_even) {
+  return h2_to_u32(u32_to_h2(nz_even) + half2v{(_Float16)960.f, (_Float16)960.f});
 }
 
 // half2 (-(1024 + z), -(1024 + z)) for one byte z (bits 0..7 of zb).
