@@ -88,11 +88,15 @@ __device__ __forceinline__ uint32_t v_code_pair(u32x2 c8, uint32_t c8s, int m) {
   return nibbles_to_biased_h2(c8[0], c8s, m);
 }
 
-// Raw bytes of one 32-token step held by one lane.
-struct StepData {
+// Raw bytes of one 32-token step held by one lane: the K part (scores) and
+// the V part (PV) are separate buffers because the loop consumes them one
+// step apart.
+struct KData {
   u32x4 kc[2][2];   // K codes of the lane's two tokens (group lg); int4 uses [bk][0]
   uint32_t kz[2];   // K zero bytes of those tokens (group lg)
   u32x2 ks[2];      // K scales of those tokens (all 4 groups)
+};
+struct VData {
   u32x4 vw[4];      // the step's V block, 16 bytes per lane per load: load k holds bytes
                     // 1024 k + 16 L .. +15 in lane L (int8: 4 KB, four loads; int4: 2 KB, two)
   u32x2 vz;         // V zeros of the lane's 8 tokens (group i16 % 4)
@@ -162,10 +166,9 @@ __device__ __forceinline__ Rsrc make_rsrcs(const Ptrs& p) {
   return r;
 }
 
-// Loads of one 32-token step starting at t0 (a multiple of 32).
+// Loads of one 32-token step starting at t0 (a multiple of 32): K part.
 template <bool K8, bool V8>
-__device__ __forceinline__ void load_step(const Rsrc& r, int t0, const LaneOffsets& o,
-                                          StepData& s) {
+__device__ __forceinline__ void load_k(const Rsrc& r, int t0, const LaneOffsets& o, KData& s) {
   const int tk = t0 * (K8 ? D : D / 2);
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk) {
@@ -174,17 +177,31 @@ __device__ __forceinline__ void load_step(const Rsrc& r, int t0, const LaneOffse
     s.kz[bk] = __builtin_amdgcn_raw_buffer_load_b8(r.kz, o.kz[bk], t0 * 4, 0);
     s.ks[bk] = __builtin_amdgcn_raw_buffer_load_b64(r.ks, o.ks[bk], t0 * 8, 0);
   }
-  // one V block of D channel rows per step; load db covers rows 16 db .. +15,
-  // one contiguous 256 (int4) / 512 (int8) byte run per instruction
+}
+
+// V part: one V block of D channel rows per step, read as 16-byte loads over
+// the contiguous block (the memory pipeline's instruction rate, not its
+// bandwidth, limited the step with one 4- or 8-byte operand piece per load);
+// step_pv redistributes it through LDS.
+template <bool V8>
+__device__ __forceinline__ void load_v(const Rsrc& r, int t0, const LaneOffsets& o, VData& s) {
   const int tv = (t0 >> 5) * (D * (V8 ? 32 : 16));
-  // 16-byte loads over the contiguous block (the memory pipeline's
-  // instruction rate, not its bandwidth, limited the step with one 4- or
-  // 8-byte operand piece per load); compute_step redistributes through LDS
 #pragma unroll
   for (int k = 0; k < (V8 ? 4 : 2); ++k)
     s.vw[k] = __builtin_amdgcn_raw_buffer_load_b128(r.v, o.vrow + 1024 * k, tv, 0);
   s.vz = __builtin_amdgcn_raw_buffer_load_b64(r.vz, o.vz, t0, 0);
   s.vs = __builtin_amdgcn_raw_buffer_load_b128(r.vs, o.vs, 2 * t0, 0);
+}
+
+// A step with fewer than STEP live tokens (only a wave's last step can be
+// one): zero the V scales of the dead tokens, so their V-hat is exactly 0
+// whatever the cache holds there.
+__device__ __forceinline__ void mask_v_tail(VData& s, int nvalid, int lg) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ta = 8 * lg + 2 * j;
+    s.vs[j] &= (ta < nvalid ? 0x0000FFFFu : 0u) | (ta + 1 < nvalid ? 0xFFFF0000u : 0u);
+  }
 }
 
 template <int R, bool K8, bool V8>
@@ -229,10 +246,14 @@ __device__ __forceinline__ void pv_group(f32x4 (&acc)[8], const u32x2 (&vc)[8],
   }
 }
 
+// Scores and softmax of one step: the running maximum and normaliser are
+// updated, the weights come back as the PV operand (bp), and the return value
+// says whether the accumulator must be rescaled by `alpha` (rare: see
+// rescale_acc) before the step's PV is added.
 template <int R, bool K8, bool V8, int MODE>
-__device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K8, V8>& ws,
-                                             StepData& s, int nvalid, int i16, int lg,
-                                             uint32_t* vst) {
+__device__ __forceinline__ bool step_scores(const DecodeArgs& a, WaveState<R, K8, V8>& ws,
+                                            const KData& s, int nvalid, int i16, int lg,
+                                            half8& bp, float (&alpha)[(R + 3) / 4]) {
   constexpr int NRB = WaveState<R, K8, V8>::NRB;
   // ---------------- scores ----------------
   float sc[NRB][2];
@@ -286,29 +307,21 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
       sc[rb][bk] = live ? x : 0.f;
     }
   }
-  // The chunk's last step may hold fewer than STEP tokens (wave-uniform and
-  // rare, so a real branch rather than selects on every step): tokens past
-  // the end get score -inf and a zero V scale, so their weight and their
-  // V-hat are exactly 0 whatever the cache holds there.
-  if (nvalid < STEP) {
-    asm volatile("" ::: "memory");
+  // The chunk's last step may hold fewer than STEP tokens: tokens past the
+  // end get score -inf (a select, so that no branch splits the step from the
+  // PV work it is scheduled with), hence weight exactly 0.
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
-      if (qk_token<V8>(bk, i16) >= nvalid)
+  for (int bk = 0; bk < 2; ++bk) {
+    const bool dead = qk_token<V8>(bk, i16) >= nvalid;
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) sc[rb][bk] = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ta = 8 * lg + 2 * j;
-      s.vs[j] &= (ta < nvalid ? 0x0000FFFFu : 0u) | (ta + 1 < nvalid ? 0xFFFF0000u : 0u);
-    }
+    for (int rb = 0; rb < NRB; ++rb) sc[rb][bk] = dead ? -INFINITY : sc[rb][bk];
   }
 
   if constexpr (MODE == MAX_PASS) {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
       ws.m_run[rb] = fmaxf(ws.m_run[rb], row16_max(fmaxf(sc[rb][0], sc[rb][1])));
-    return;
+    return false;
   }
 
   // ---------------- online softmax ----------------
@@ -318,7 +331,6 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
   // final O = acc / l is unchanged by the choice of m.  With FIXED_MAX, m is
   // the global maximum from pass 1 and never moves (weights <= 1).
   uint32_t p2[NRB];
-  float alpha[NRB];
   bool any_move = false;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
@@ -357,20 +369,31 @@ __device__ __forceinline__ void compute_step(const DecodeArgs& a, WaveState<R, K
     // accumulator columns are never written out
     pb[mm] = v;
   }
-  if (rescale) {
-    // rare: keep it a real branch (an empty volatile asm stops the compiler
-    // from turning it into an unconditional multiply by a selected factor)
-    asm volatile("" ::: "memory");
-    float al = lane_read_f(alpha[0], hsrc);
-    if (NRB > 1) {
-      const float a1 = lane_read_f(alpha[NRB - 1], hsrc);
-      al = (hcol >> 2) ? a1 : al;
-    }
-#pragma unroll
-    for (int db = 0; db < 8; ++db) ws.acc[db] = ws.acc[db] * al;
-  }
-  const half8 bp = u4_to_h8(pb);
+  bp = u4_to_h8(pb);
+  return rescale;
+}
 
+// acc *= alpha of its query head (accumulator column = head), gathered from
+// the score layout.
+template <int R, bool K8, bool V8>
+__device__ __forceinline__ void rescale_acc(WaveState<R, K8, V8>& ws,
+                                            const float (&alpha)[(R + 3) / 4], int i16) {
+  constexpr int NRB = (R + 3) / 4;
+  const int hsrc = (i16 & 3) * 16;
+  float al = lane_read_f(alpha[0], hsrc);
+  if (NRB > 1) {
+    const float a1 = lane_read_f(alpha[NRB - 1], hsrc);
+    al = (i16 >> 2) ? a1 : al;
+  }
+#pragma unroll
+  for (int db = 0; db < 8; ++db) ws.acc[db] = ws.acc[db] * al;
+}
+
+// PV of one step: the V-hat^T operand is built from the step's V block and
+// multiplied with the weights bp.
+template <int R, bool K8, bool V8>
+__device__ __forceinline__ void step_pv(WaveState<R, K8, V8>& ws, const VData& s, half8 bp,
+                                        int i16, int lg, uint32_t* vst) {
   // ---------------- V-hat^T operand and PV ----------------
   // loads 2 gq and 2 gq + 1 are channels of group gq
   // V codes in the operand layout: lane (i16, lg) takes row 16 db + i16,
@@ -505,34 +528,66 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
     return (tile0 + k + __builtin_ctz(rest)) << 7;
   };
 
-  // ---- two-buffer pipeline over the wave's steps -----------------------------
-  // The loads of the next step are issued before the current step is
-  // computed.  Every iteration issues exactly one step of loads (past the end:
-  // a repeat of a valid step that is never used), so the number of loads in
-  // flight is the same on every path and each wait before a use is partial.
-  // (A third buffer measured no faster: the loop is bound by its compute.)
-  // Step starts are wave-uniform: keep them scalar (they are the scalar
-  // offsets of the buffer loads).
+  // ---- software pipeline over the wave's steps -------------------------------
+  // Iteration i issues the K loads of step i+2 and the V loads of step i+1,
+  // then computes the PV of step i together with the scores and softmax of
+  // step i+1 in one block (independent work the scheduler interleaves, so the
+  // latencies of one chain hide behind the other).  The rare branches (tail
+  // V scales of step i before, accumulator rescale for step i+1 after) sit
+  // outside the block; the rescale after PV(i) is exact since PV(i) is
+  // relative to the old maximum.  Every iteration issues exactly one step of
+  // loads (past the end: a repeat of a valid step that is never used), so each
+  // wait before a use is partial.  Step starts are wave-uniform: keep them
+  // scalar (they are the scalar offsets of the buffer loads).
   auto addr = [&](int t) { return __builtin_amdgcn_readfirstlane(t < t_end ? t : t_safe); };
   const LaneOffsets lo = lane_offsets<K8, V8>(i16, lg, p.cap);
   const Rsrc rs = make_rsrcs<K8, V8>(p);
-  StepData A, Bf;
-  int t_cur = next_step(t_begin);
-  if (t_cur < t_end) {
-    load_step<K8, V8>(rs, addr(t_cur), lo, A);
-    int t_nxt = next_step(t_cur + STEP);
-    load_step<K8, V8>(rs, addr(t_nxt), lo, Bf);
-    while (true) {
-      compute_step<R, K8, V8, MODE>(a, ws, A, t_end - t_cur, i16, lg, vst);
-      t_cur = t_nxt;
-      if (t_cur >= t_end) break;
-      t_nxt = next_step(t_cur + STEP);
-      load_step<K8, V8>(rs, addr(t_nxt), lo, A);
-      compute_step<R, K8, V8, MODE>(a, ws, Bf, t_end - t_cur, i16, lg, vst);
-      t_cur = t_nxt;
-      if (t_cur >= t_end) break;
-      t_nxt = next_step(t_cur + STEP);
-      load_step<K8, V8>(rs, addr(t_nxt), lo, Bf);
+  int tc = next_step(t_begin);
+  if (tc < t_end) {
+    int tn = next_step(tc + STEP);
+    KData K0, K1;
+    VData V0, V1;
+    half8 bp;
+    float alpha[NRB];
+    load_k<K8, V8>(rs, addr(tc), lo, K0);
+    if (MODE != MAX_PASS) load_v<V8>(rs, addr(tc), lo, V0);
+    load_k<K8, V8>(rs, addr(tn), lo, K1);
+    if (step_scores<R, K8, V8, MODE>(a, ws, K0, t_end - tc, i16, lg, bp, alpha)) {
+      asm volatile("" ::: "memory");
+      rescale_acc(ws, alpha, i16);
+    }
+    // V(tc) in Va, K(tn) in Kb, bp = weights of step tc; Ka and Vb are free
+    auto body = [&](KData& Ka, const KData& Kb, VData& Va, VData& Vb) -> bool {
+      if (tn >= t_end) {
+        if (MODE != MAX_PASS) {
+          if (t_end - tc < STEP) {
+            asm volatile("" ::: "memory");
+            mask_v_tail(Va, t_end - tc, lg);
+          }
+          step_pv(ws, Va, bp, i16, lg, vst);
+        }
+        return false;
+      }
+      const int t2 = next_step(tn + STEP);
+      load_k<K8, V8>(rs, addr(t2), lo, Ka);
+      if (MODE != MAX_PASS) {
+        load_v<V8>(rs, addr(tn), lo, Vb);
+        if (t_end - tc < STEP) {
+          asm volatile("" ::: "memory");
+          mask_v_tail(Va, t_end - tc, lg);
+        }
+        step_pv(ws, Va, bp, i16, lg, vst);
+      }
+      const bool rs_ = step_scores<R, K8, V8, MODE>(a, ws, Kb, t_end - tn, i16, lg, bp, alpha);
+      if (rs_) {
+        asm volatile("" ::: "memory");
+        rescale_acc(ws, alpha, i16);
+      }
+      tc = tn;
+      tn = t2;
+      return true;
+    };
+    while (body(K0, K1, V0, V1) && body(K1, K0, V1, V0)) {
     }
   }
 
