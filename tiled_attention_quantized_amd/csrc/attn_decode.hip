@@ -673,8 +673,11 @@ decode_split_kernel(DecodeArgs a) {
   const int u = blockIdx.x / a.nchunk;
   const int c = blockIdx.x - u * a.nchunk;
 #else
-  const int c = blockIdx.x / units;
-  const int u = blockIdx.x - c * units;
+  // highest chunk index first: the later chunks exist only for the longest
+  // sequences, so they start early and the short final chunks fill the end
+  // (ragged lengths: 238 -> 235 us)
+  const int c = a.nchunk - 1 - (int)(blockIdx.x / units);
+  const int u = blockIdx.x - (a.nchunk - 1 - c) * units;
 #endif
   const int b = u / a.nheads;
   const int g = a.heads[u - b * a.nheads];
