@@ -61,7 +61,9 @@ pool_q_kernel(MaskGenArgs a) {
   for (int hl = 0; hl < a.r; ++hl) {
     const uint16_t* qp = a.q + (((int64_t)b * a.Hq + g * a.r + hl) * a.L) * 128 + 8 * c8;
     for (int row = lo + kr; row < hi; row += 16) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(qp + (int64_t)row * 128);
+      // Q is read once here: non-temporal (keeps the caches for the K
+      // pooling; 128K prompt: 451 -> 416 us for the whole generator)
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qp + (int64_t)row * 128));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const half2v h = u32_to_h2(w[e]);
