@@ -71,6 +71,31 @@ def test_decode_with_tile_mask(bits):
     assert not got[2].any()
 
 
+def test_decode_multistep_waves_with_mask():
+    """Shapes whose split uses 1024-token chunks (8 steps of 32 tokens per
+    wave), so the step pipeline runs with its buffers in rotation: ragged odd
+    lengths (a partial last step), a KV-tile mask that drops tiles inside a
+    wave's range (steps skipped mid-range), int8 and int4 heads."""
+    require_gpu()
+    spec = W.small("decode", B=16, Hq=32, Hkv=8, ragged=(9001, 16383), bits=4,
+                   n_int8_heads=2, seed=77, capacity=16384)
+    inp = W.make_inputs(spec)
+    kc = T.KVCache(spec.B, spec.Hkv, spec.D, spec.cap, inp.structure.head_bits, T.LAYOUT_TOKEN)
+    ws_bytes = T.decode_workspace_bytes(kc, spec.Hq, spec.max_len)
+    del kc
+    nchunk = ws_bytes // (spec.B * spec.Hq * (128 + 2) * 4)
+    chunk = -(-spec.max_len // nchunk)
+    assert chunk >= 1024, chunk          # several steps per wave
+    nk = spec.cap // 128
+    rng = np.random.default_rng(7)
+    mask = (rng.random((spec.B, nk)) < 0.7).astype(np.uint8)
+    mask[:, 0] = 1
+    note(f"decode multi-step waves, chunk {chunk}, lens {inp.structure.seq_lens.tolist()}")
+    got, want, _ = run_decode(inp, mask=mask, workers=8)
+    err = max_abs(got, want)
+    assert err <= TOL, err
+
+
 def test_decode_zero_length_and_uniform_v():
     require_gpu()
     spec = W.small("decode", B=3, Hq=4, Hkv=1, ragged=(1, 400), bits=8, seed=9)
