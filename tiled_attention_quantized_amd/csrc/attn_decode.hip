@@ -11,11 +11,11 @@
 //  * one workgroup per (KV chunk, KV head, batch); a 256-thread workgroup owns one chunk
 //    of `chunk` tokens of one (batch, KV head) and serves all r = Hq/Hkv query
 //    heads of that KV head, so each K/V byte is read once.
-//  * each of the 4 waves streams chunk/4 tokens in steps of 32 tokens and keeps
-//    its own (max, normaliser, accumulator).  The loads of the next step are
-//    issued before the current step is computed (register double buffering).
-//    The waves merge through LDS and the workgroup writes one partial triple
-//    per query head.
+//  * the 4 waves share the chunk in steps of 32 tokens (wave w takes step w of
+//    every 128-token tile) and each keeps its own (max, normaliser,
+//    accumulator).  The loads of the next steps are issued before the current
+//    step is computed (software pipeline over the steps).  The waves merge
+//    through LDS and the workgroup writes one partial triple per query head.
 //  * a second kernel merges the chunk partials of each (batch, query head) in
 //    chunk order and writes fp16 O.
 //  * two-pass variant (the literal reading of the "coarse max first, then fix
@@ -510,31 +510,34 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
 #pragma unroll
   for (int db = 0; db < 8; ++db) ws.acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int per_wave = a.chunk / WAVES;
-  const int t_begin = c * a.chunk + w * per_wave;
-  const int t_end = min(t_begin + per_wave, n);
-  const int t_safe = c * a.chunk;   // a valid step address (c * chunk < n)
+  // The waves share the chunk: wave w takes the 32-token step w of every
+  // 128-token tile, so a partial last chunk of a sequence keeps all four waves
+  // busy (with contiguous quarters, most of its waves idled while one ran its
+  // full range) and the workgroup reads one contiguous stream.
+  const int c0 = c * a.chunk;
+  const int t_end = min(c0 + a.chunk, n);
+  const int t_safe = c0;   // a valid step address (c * chunk < n)
 
-  // KV-tile keep bits of the tiles this wave touches (at most 9 tiles of 128
-  // tokens), read once so that the step loop does no mask loads.
-  const int tile0 = t_begin >> 7;
+  // KV-tile keep bits of the chunk's tiles (chunk <= 4096: at most 32 tiles of
+  // 128 tokens), read once so that the step loop does no mask loads.
   uint32_t tbits = 0xFFFFFFFFu;
-  if (a.mask && t_begin < t_end) {
-    const uint8_t* mrow = a.mask + (int64_t)b * a.mask_sb + (int64_t)g * a.mask_sh;
-    const int tile1 = (t_end - 1) >> 7;
+  if (a.mask) {
+    const uint8_t* mrow = a.mask + (int64_t)b * a.mask_sb + (int64_t)g * a.mask_sh + (c0 >> 7);
+    const int ntile = (t_end - c0 + 127) >> 7;
     tbits = 0;
-    for (int k = 0; k <= tile1 - tile0; ++k) tbits |= (mrow[tile0 + k] ? 1u : 0u) << k;
+    for (int k = 0; k < ntile; ++k) tbits |= (mrow[k] ? 1u : 0u) << k;
   }
-  // first step at or after t whose tile is kept (t_end if none): a find-first-
-  // set on the wave-uniform keep bits, no loop
+  // first of this wave's steps at or after t (t itself one of them) whose
+  // tile is kept (t_end if none): a find-first-set on the wave-uniform keep
+  // bits, no loop
   auto next_step = [&](int t) -> int {
     if (t >= t_end) return t;
-    const int k = (t >> 7) - tile0;
-    const uint32_t rest = tbits >> k;
+    const uint32_t rest = tbits >> ((t - c0) >> 7);
     if (rest & 1u) return t;
     if (rest == 0u) return t_end;
-    return (tile0 + k + __builtin_ctz(rest)) << 7;
+    return t + (__builtin_ctz(rest) << 7);
   };
+  constexpr int STRIDE = STEP * WAVES;   // from one of a wave's steps to the next
 
   // ---- software pipeline over the wave's steps -------------------------------
   // Iteration i issues the K loads of step i+2 and the V loads of step i+1,
@@ -550,9 +553,9 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
   auto addr = [&](int t) { return __builtin_amdgcn_readfirstlane(t < t_end ? t : t_safe); };
   const LaneOffsets lo = lane_offsets<K8, V8>(i16, lg, p.cap);
   const Rsrc rs = make_rsrcs<K8, V8>(p);
-  int tc = next_step(t_begin);
+  int tc = next_step(c0 + w * STEP);
   if (tc < t_end) {
-    int tn = next_step(tc + STEP);
+    int tn = next_step(tc + STRIDE);
     KData K0, K1;
     VData V0, V1;
     half8 bp;
@@ -576,7 +579,7 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
         }
         return false;
       }
-      const int t2 = next_step(tn + STEP);
+      const int t2 = next_step(tn + STRIDE);
       load_k<K8, V8>(rs, addr(t2), lo, Ka);
       if (MODE != MAX_PASS) {
         load_v<V8>(rs, addr(tn), lo, Vb);
