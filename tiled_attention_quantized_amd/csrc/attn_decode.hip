@@ -134,7 +134,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int i16, int lg, int cap) {
     o.ks[bk] = T * 8;                                      // 4 fp16 scales per token
   }
   // lanes i16 = 0..3 of each row hold the row's tokens' scales and zeros of
-  // groups 0..3 (the other lanes repeat them); compute_step broadcasts them
+  // groups 0..3 (the other lanes repeat them); step_pv broadcasts them
   o.vz = (uint32_t)(i16 & 3) * (uint32_t)cap + 8 * lg;
   o.vs = 2 * o.vz;
   o.vrow = 16u * (uint32_t)(16 * lg + i16);
