@@ -96,6 +96,57 @@ def test_decode_multistep_waves_with_mask():
     assert err <= TOL, err
 
 
+def _decode_chunk(kc, hq, max_len, B):
+    ws = T.decode_workspace_bytes(kc, hq, max_len)
+    nchunk = ws // (B * hq * (128 + 2) * 4)
+    return -(-max_len // nchunk)
+
+
+def test_decode_split_count_and_key_permutation_invariance():
+    """The same inputs decoded under two split geometries (a larger
+    max_seq_len selects longer chunks), and with the tokens of every sequence
+    permuted before quantisation (codes are per token, so the exact result is
+    unchanged): each agrees with the oracle and with the others within the
+    bar."""
+    require_gpu()
+    spec = W.small("decode", B=16, Hq=32, Hkv=8, ragged=(1500, 4000), bits=4,
+                   n_int8_heads=3, seed=91, capacity=16384)
+    inp = W.make_inputs(spec)
+    st = inp.structure
+    bits = st.head_bits
+    kc = gpu_cache(inp.k, bits, T.LAYOUT_TOKEN, spec.cap)
+    vc = gpu_cache(inp.v, bits, T.LAYOUT_CHANNEL, spec.cap)
+    q = torch.from_numpy(inp.q).cuda()
+    lens = lens_tensor(st.seq_lens)
+    short, long_ = 4096, spec.cap
+    c_short = _decode_chunk(kc, spec.Hq, short, spec.B)
+    c_long = _decode_chunk(kc, spec.Hq, long_, spec.B)
+    assert c_short != c_long, (c_short, c_long)
+    note(f"decode split invariance: chunks {c_short} and {c_long}")
+    a = T.attn_decode(kc, vc, q, lens, short).cpu().numpy().astype(np.float64)
+    b = T.attn_decode(kc, vc, q, lens, long_).cpu().numpy().astype(np.float64)
+    # permuted tokens within each sequence
+    rng = np.random.default_rng(3)
+    kp, vp = inp.k.copy(), inp.v.copy()
+    for bb in range(spec.B):
+        n = int(st.seq_lens[bb])
+        perm = rng.permutation(n)
+        kp[bb, :, :n] = inp.k[bb][:, perm]
+        vp[bb, :, :n] = inp.v[bb][:, perm]
+    del kc, vc
+    kcp = gpu_cache(kp, bits, T.LAYOUT_TOKEN, spec.cap)
+    vcp = gpu_cache(vp, bits, T.LAYOUT_CHANNEL, spec.cap)
+    c = T.attn_decode(kcp, vcp, q, lens, short).cpu().numpy().astype(np.float64)
+    okc = oq.build_cache(inp.k, bits, "token", cap=spec.cap)
+    ovc = oq.build_cache(inp.v, bits, "channel", cap=spec.cap)
+    want = oa.decode(inp.q, oq.dequantized_all(okc), oq.dequantized_all(ovc), st.seq_lens,
+                     workers=8)
+    for got in (a, b, c):
+        assert max_abs(got, want) <= TOL
+    assert max_abs(a, b) <= TOL
+    assert max_abs(a, c) <= TOL
+
+
 def test_decode_zero_length_and_uniform_v():
     require_gpu()
     spec = W.small("decode", B=3, Hq=4, Hkv=1, ragged=(1, 400), bits=8, seed=9)
