@@ -280,6 +280,7 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
     return false;
   };
   auto next_tile = [&](int kt) -> int {
+    if (mb == nullptr) return kt;   // dense: every tile below nkt is needed
     while (kt < nkt && !wg_needs(kt)) ++kt;
     return kt;
   };
@@ -298,6 +299,10 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
 
   // ---- LDS stage helpers ---------------------------------------------------------
   auto stage_ptr = [&](int j) -> char* { return lds + (j % 3) * LDS_STAGE; };
+  // ring stage after / before stage x (x in 0..2)
+  auto ring_next = [](int x) { return x == 2 ? 0 : x + 1; };
+  auto ring_prev = [](int x) { return x == 0 ? 2 : x - 1; };
+  auto stage_at = [&](int x) -> char* { return lds + x * LDS_STAGE; };
   // S^T = K-hat Q^T for the tile in stage j (16 MFMAs)
   auto qk = [&](int j, f32x16* S) {
     const uint8_t* kl = reinterpret_cast<const uint8_t*>(stage_ptr(j));
@@ -351,7 +356,7 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
     f32x16 S0[2], S1[2];
     qk(0, S0);
     int tj = t0_, tj1 = t1_, tj2 = t2_;
-    int j = 0;
+    int j3 = 0;   // ring stage of tile j
 
     auto iteration = [&](f32x16* Sc, f32x16* Sn) {
       const int tj3 = tj2 < nkt ? next_tile(tj2 + 1) : nkt;
@@ -393,7 +398,7 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
       // operand is read PF_RA MFMAs ahead; the weights of elements 2i, 2i+1 of
       // S(j) are computed behind it.  Past the last tile the MFMAs recompute
       // a resident stage (result unused).
-      const uint8_t* kl = reinterpret_cast<const uint8_t*>(stage_ptr(j + 1));
+      const uint8_t* kl = reinterpret_cast<const uint8_t*>(stage_at(ring_next(j3)));
       auto kread = [&](int i) -> u32x4 {
         const int kb = i & 1, ks = i >> 1;
         return *reinterpret_cast<const u32x4*>(kl + (32 * kb + i32) * KS_STRIDE + (16 * ks + 8 * hb) * 2);
@@ -439,12 +444,12 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
       // MFMA i uses accumulator db = i % 4 and k-step kk = i / 4; pair i of the
       // staged tile (K pairs 0..7, then V pairs 0..7) is dequantised behind it.
       {
-        const uint8_t* vl = reinterpret_cast<const uint8_t*>(stage_ptr(j)) + LDS_K;
+        const uint8_t* vl = reinterpret_cast<const uint8_t*>(stage_at(j3)) + LDS_K;
         auto vread = [&](int i) -> u32x4 {
           const int db = i & 3, kk = i >> 2;
           return *reinterpret_cast<const u32x4*>(vl + (32 * db + i32) * VS_STRIDE + (16 * kk + 8 * hb) * 2);
         };
-        char* sdst = stage_ptr(j + 2);
+        char* sdst = stage_at(ring_prev(j3));
         const int unit = tid >> 1, khalf = tid & 1;
         const int kkey = unit >> 2, kgrp = unit & 3;
         const int vd = tid >> 2, vq = tid & 3;
@@ -492,7 +497,7 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
       }
       stage_load<K8, V8>(c, (tj3 < nkt ? tj3 : t0_) * KT, st);
       tj = tj1; tj1 = tj2; tj2 = tj3;
-      ++j;
+      j3 = ring_next(j3);
     };
 
     while (true) {
