@@ -139,6 +139,18 @@ size_t taq_kv_meta_count(const taq_kv_cache* cache);
 taq_status taq_kv_quantize(const taq_kv_cache* cache, const void* x_f16,
                            int32_t start, int32_t count, void* stream);
 
+/* The same quantisation for the K and the V cache of a layer in one launch:
+ * xk into k_cache and xv into v_cache (each fp16 [B][Hkv][count][D] of its
+ * own cache's shape), tokens start .. start+count-1 of both; the two caches
+ * are quantised side by side instead of one after the other.  Results are
+ * byte-identical to two taq_kv_quantize calls.  Both caches must have the same
+ * head_dim (their layouts, bits and shapes may differ); the token range must
+ * lie inside both capacities.  Errors: as taq_kv_quantize for either cache,
+ * plus INVALID_ARGUMENT when the head_dims differ. */
+taq_status taq_kv_quantize_pair(const taq_kv_cache* k_cache, const taq_kv_cache* v_cache,
+                                const void* xk_f16, const void* xv_f16, int32_t start,
+                                int32_t count, void* stream);
+
 /* Quantise-on-append: the same quantisation, batch entry b's fp16 tokens
  * x[b][h][0 .. count-1] going to cache positions starts[b] .. starts[b] +
  * count - 1, so sequences of different lengths each append their next chunk

@@ -84,6 +84,24 @@ def test_quantize_range_and_pointer_checks():
     assert L.taq_kv_dequantize(ctypes.byref(d), 0, 2, FAKE + 8, None, None) == MISALIGNED
 
 
+def test_quantize_pair_rejects():
+    L = T.lib()
+    k = cache(layout=0)
+    v = cache(layout=1)
+
+    def call(k=k, v=v, xk=FAKE, xv=FAKE, start=0, count=4):
+        return status_of(L.taq_kv_quantize_pair(ctypes.byref(k), ctypes.byref(v), xk, xv, start,
+                                                count, None))
+    assert call(v=cache(D=64, layout=1))[0] == INVALID           # head_dims differ
+    assert call(xk=0)[0] == INVALID
+    assert call(xv=0)[0] == INVALID
+    assert call(xv=FAKE + 2)[0] == MISALIGNED
+    assert call(start=250, count=7)[0] == INVALID                # past the capacity
+    assert call(v=cache(cap=128, layout=1), start=120, count=16)[0] == INVALID
+    assert call(k=cache(group=16))[0] == UNSUPPORTED             # either cache is checked
+    assert call(v=cache(bits=(8, 5), layout=1))[0] != 0
+
+
 def decode_call(k=None, v=None, hq=8, max_len=200, mask=None, ws_bytes=1 << 30,
                 q=FAKE, o=FAKE, lens=FAKE, ws=FAKE, scale=0.0):
     k = k or cache(B=1, H=2, cap=256, bits=(8, 8), layout=0)

@@ -95,3 +95,35 @@ def test_quantize_decode_workload_head_mix_outliers():
         gc = gpu_cache(inp.k, bits, layout, spec.cap)
         oc = oracle_cache(inp.k, bits, lname, spec.cap)
         assert_cache_equal(gc, oc)
+
+
+@pytest.mark.parametrize("layouts", [(T.LAYOUT_TOKEN, T.LAYOUT_CHANNEL),
+                                     (T.LAYOUT_CHANNEL, T.LAYOUT_CHANNEL),
+                                     (T.LAYOUT_TOKEN, T.LAYOUT_TOKEN)])
+def test_quantize_pair_equals_two_calls(layouts):
+    """kv_quantize_pair (both caches in one launch) writes the bytes of two
+    kv_quantize calls and of the oracle, over a range cut at odd positions,
+    with different per-head bits for the two caches."""
+    require_gpu()
+    rng = np.random.default_rng(31 + layouts[0] * 2 + layouts[1])
+    B, H, D, cap = 2, 3, 128, 384
+    names = {T.LAYOUT_TOKEN: "token", T.LAYOUT_CHANNEL: "channel"}
+    kb, vb = (8, 4, 4), (4, 8, 4)
+    xk = adversarial(rng, B, H, cap, D)
+    xv = adversarial(rng, B, H, cap, D)
+    note(f"kv_quantize_pair layouts={layouts}")
+    pk, pv = T.KVCache(B, H, D, cap, kb, layouts[0]), T.KVCache(B, H, D, cap, vb, layouts[1])
+    sk, sv = T.KVCache(B, H, D, cap, kb, layouts[0]), T.KVCache(B, H, D, cap, vb, layouts[1])
+    tk, tv = torch.from_numpy(xk).cuda(), torch.from_numpy(xv).cuda()
+    for s0, s1 in ((0, 33), (33, 97), (97, 384)):
+        ak, av = tk[:, :, s0:s1].contiguous(), tv[:, :, s0:s1].contiguous()
+        T.kv_quantize_pair(pk, pv, ak, av, s0)
+        T.kv_quantize(sk, ak, s0)
+        T.kv_quantize(sv, av, s0)
+    torch.cuda.synchronize()
+    for a, b in ((pk, sk), (pv, sv)):
+        assert torch.equal(a.codes, b.codes)
+        assert torch.equal(a.scales, b.scales)
+        assert torch.equal(a.zeros, b.zeros)
+    assert_cache_equal(pk, oracle_cache(xk, kb, names[layouts[0]], cap))
+    assert_cache_equal(pv, oracle_cache(xv, vb, names[layouts[1]], cap))

@@ -34,7 +34,7 @@ EXPORTS = ("taq_last_error", "taq_abi_version", "taq_device_check",
            "taq_kv_append", "taq_attn_prefill_chunk", "taq_tile_mask_workspace_bytes",
            "taq_tile_mask_generate", "taq_attn_decode_two_pass",
            "taq_head_sensitivity_workspace_bytes", "taq_head_sensitivity",
-           "taq_attn_prefill_chunk_workspace_bytes")
+           "taq_attn_prefill_chunk_workspace_bytes", "taq_kv_quantize_pair")
 
 
 class TaqError(RuntimeError):
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
         "taq_kv_codes_bytes": (SZ, [CP]),
         "taq_kv_meta_count": (SZ, [CP]),
         "taq_kv_quantize": (ctypes.c_int, [CP, P, I32, I32, P]),
+        "taq_kv_quantize_pair": (ctypes.c_int, [CP, CP, P, P, I32, I32, P]),
         "taq_kv_dequantize": (ctypes.c_int, [CP, I32, I32, P, P, P]),
         "taq_attn_decode_workspace_bytes": (SZ, [CP, I32, I32]),
         "taq_attn_decode": (ctypes.c_int, [CP, CP, P, I32, P, I32, MP, F, P, P, SZ, P]),
@@ -185,6 +186,23 @@ def kv_quantize(cache: KVCache, x, start: int = 0) -> None:
         raise ValueError("x shape does not match the cache")
     d = cache.desc()
     _check(lib().taq_kv_quantize(ctypes.byref(d), _ptr(x), start, S, _stream(x.device)))
+
+
+def kv_quantize_pair(k: KVCache, v: KVCache, xk, xv, start: int = 0) -> None:
+    """Quantise fp16 xk and xv [B][Hkv][S][D] into tokens start .. start+S-1 of
+    the K and V caches in one launch (byte-identical to two kv_quantize calls)."""
+    import torch
+    for cache, x in ((k, xk), (v, xv)):
+        if x.dtype != torch.float16 or not x.is_contiguous() or x.dim() != 4:
+            raise ValueError("xk and xv must be contiguous fp16 [B][Hkv][S][D] tensors")
+        B, H, S, D = x.shape
+        if (B, H, D) != (cache.batch, cache.num_kv_heads, cache.head_dim):
+            raise ValueError("x shape does not match its cache")
+    if xk.shape[2] != xv.shape[2]:
+        raise ValueError("xk and xv must hold the same number of tokens")
+    kd, vd = k.desc(), v.desc()
+    _check(lib().taq_kv_quantize_pair(ctypes.byref(kd), ctypes.byref(vd), _ptr(xk), _ptr(xv),
+                                      start, xk.shape[2], _stream(xk.device)))
 
 
 def kv_append(cache: KVCache, x, starts) -> None:

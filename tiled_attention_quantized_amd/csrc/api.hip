@@ -205,6 +205,37 @@ taq_status taq_kv_quantize(const taq_kv_cache* c, const void* x, int32_t start,
   return e == hipSuccess ? TAQ_OK : hip_fail(e, "kv_quantize launch");
 }
 
+taq_status taq_kv_quantize_pair(const taq_kv_cache* k, const taq_kv_cache* v, const void* xk,
+                                const void* xv, int32_t start, int32_t count, void* stream) {
+  taq_status st = check_cache(k, "k_cache", -1, false);
+  if (st) return st;
+  st = check_cache(v, "v_cache", -1, false);
+  if (st) return st;
+  if (k->head_dim != v->head_dim)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "k and v head_dim differ (%d, %d)", k->head_dim,
+                v->head_dim);
+  if (!xk || !xv) return fail(TAQ_ERR_INVALID_ARGUMENT, "xk or xv: null");
+  if (!aligned16(xk) || !aligned16(xv))
+    return fail(TAQ_ERR_MISALIGNED, "xk and xv must be 16-byte aligned");
+  const int32_t cap = k->capacity < v->capacity ? k->capacity : v->capacity;
+  if (start < 0 || count < 0 || (int64_t)start + count > cap)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "tokens [%d, %d + %d) outside capacity %d", start,
+                start, count, cap);
+  st = device_ok();
+  if (st) return st;
+  taq::QuantArgs a0, a1;
+  std::memset(&a0, 0, sizeof(a0));
+  std::memset(&a1, 0, sizeof(a1));
+  a0.c = geom_of(k);
+  a0.x = static_cast<const uint16_t*>(xk);
+  a1.c = geom_of(v);
+  a1.x = static_cast<const uint16_t*>(xv);
+  a0.start = a1.start = start;
+  a0.count = a1.count = count;
+  hipError_t e = taq::launch_kv_quantize_pair(a0, a1, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TAQ_OK : hip_fail(e, "kv_quantize_pair launch");
+}
+
 taq_status taq_kv_dequantize(const taq_kv_cache* c, int32_t start, int32_t count,
                              float* out32, void* out16, void* stream) {
   taq_status st = check_cache(c, "cache", -1, false);

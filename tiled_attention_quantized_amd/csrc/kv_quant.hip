@@ -116,12 +116,12 @@ __device__ __forceinline__ int head_bits(const CacheGeom& g, int h) {
 // same blocks as the channel layout; thread (t = tid / G, gi = tid % G)
 // quantises group gi of position 32 j + t when it lies in the written range
 // (append: per-batch start; positions outside the capacity are skipped).
-__global__ void __launch_bounds__(1024)
-quantize_token_kernel(QuantArgs a, int j0, int nblk) {
+__device__ __forceinline__ void quantize_token_block(const QuantArgs& a, int j0, int nblk,
+                                                     int blk) {
   const CacheGeom& g = a.c;
   const int G = g.D / 32;
-  const int jrel = blockIdx.x % nblk;
-  const int bh = blockIdx.x / nblk;
+  const int jrel = blk % nblk;
+  const int bh = blk / nblk;
   const int h = bh % g.H, b = bh / g.H;
   const int start = a.starts ? a.starts[b] : a.start;
   const int j = (a.starts ? (start >> 5) : j0) + jrel;
@@ -159,6 +159,11 @@ quantize_token_kernel(QuantArgs a, int j0, int nblk) {
   g.zeros[mi] = (uint8_t)q.zero;
 }
 
+__global__ void __launch_bounds__(1024)
+quantize_token_kernel(QuantArgs a, int j0, int nblk) {
+  quantize_token_block(a, j0, nblk, blockIdx.x);
+}
+
 // Channel layout: one workgroup of D threads per (b, h, 32-token block).
 // Thread (token t = tid / G, group gi = tid % G) quantises its group (a wave
 // reads whole token rows, contiguous), writes its scale and zero-point, and
@@ -168,14 +173,14 @@ quantize_token_kernel(QuantArgs a, int j0, int nblk) {
 // 16-byte stores.  Blocks cut by the ends of the written range write only
 // their tokens (an int4 byte shared with a token outside the range is
 // read, merged and written back).
-__global__ void __launch_bounds__(1024)
-quantize_channel_kernel(QuantArgs a, int j0, int nblk) {
-  extern __shared__ uint8_t cl_raw[];           // [D][36]: [channel][token] (+4: bank skew)
+__device__ __forceinline__ void quantize_channel_block(const QuantArgs& a, int j0, int nblk,
+                                                       int blk, uint8_t* cl_raw) {
+  // cl_raw: [D][36] bytes of LDS, [channel][token] (+4: bank skew)
   uint8_t (*cl)[36] = reinterpret_cast<uint8_t (*)[36]>(cl_raw);
   const CacheGeom& g = a.c;
   const int G = g.D / 32;
-  const int jrel = blockIdx.x % nblk;
-  const int bh = blockIdx.x / nblk;
+  const int jrel = blk % nblk;
+  const int bh = blk / nblk;
   const int h = bh % g.H, b = bh / g.H;
   const int start = a.starts ? a.starts[b] : a.start;
   const int j = (a.starts ? (start >> 5) : j0) + jrel;
@@ -236,6 +241,35 @@ quantize_channel_kernel(QuantArgs a, int j0, int nblk) {
   }
 }
 
+__global__ void __launch_bounds__(1024)
+quantize_channel_kernel(QuantArgs a, int j0, int nblk) {
+  extern __shared__ uint8_t cl_raw[];
+  quantize_channel_block(a, j0, nblk, blockIdx.x, cl_raw);
+}
+
+// Two caches of equal head_dim (K and V) in one launch: workgroups below n0
+// quantise a0's blocks, the others a1's, each with its cache's layout; the
+// two run side by side instead of one after the other.
+__global__ void __launch_bounds__(1024)
+quantize_pair_kernel(QuantArgs a0, int j00, int nblk0, int n0, QuantArgs a1, int j01,
+                     int nblk1) {
+  extern __shared__ uint8_t cl_raw[];
+  // each branch reads its own argument block directly (selecting one of the
+  // two by a runtime condition would copy them to per-thread memory)
+  const int blk = blockIdx.x;
+  if (blk < n0) {
+    if (a0.c.layout == TAQ_LAYOUT_TOKEN)
+      quantize_token_block(a0, j00, nblk0, blk);
+    else
+      quantize_channel_block(a0, j00, nblk0, blk, cl_raw);
+  } else {
+    if (a1.c.layout == TAQ_LAYOUT_TOKEN)
+      quantize_token_block(a1, j01, nblk1, blk - n0);
+    else
+      quantize_channel_block(a1, j01, nblk1, blk - n0, cl_raw);
+  }
+}
+
 // One thread per (b, h, token, group).
 __global__ void __launch_bounds__(256)
 dequantize_kernel(QuantArgs a) {
@@ -282,12 +316,30 @@ inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1)
 
 }  // namespace
 
+// 32-position blocks: the range's own, or (per-batch starts) enough blocks
+// from each start's block to cover count tokens at any alignment
+static void quant_blocks(const QuantArgs& a, int& j0, int& nblk) {
+  j0 = a.starts ? 0 : a.start / 32;
+  nblk = a.starts ? a.count / 32 + 2 : (a.start + a.count - 1) / 32 - j0 + 1;
+}
+
+hipError_t launch_kv_quantize_pair(const QuantArgs& a0, const QuantArgs& a1, hipStream_t s) {
+  if (a0.count == 0) return hipSuccess;   // both caches take the same token range
+  int j00, nblk0, j01, nblk1;
+  quant_blocks(a0, j00, nblk0);
+  quant_blocks(a1, j01, nblk1);
+  const int64_t n0 = (int64_t)a0.c.B * a0.c.H * nblk0;
+  const int64_t n1 = (int64_t)a1.c.B * a1.c.H * nblk1;
+  const bool chan = a0.c.layout != TAQ_LAYOUT_TOKEN || a1.c.layout != TAQ_LAYOUT_TOKEN;
+  hipLaunchKernelGGL(quantize_pair_kernel, dim3((unsigned)(n0 + n1)), dim3(a0.c.D),
+                     chan ? a0.c.D * 36 : 0, s, a0, j00, nblk0, (int)n0, a1, j01, nblk1);
+  return hipGetLastError();
+}
+
 hipError_t launch_kv_quantize(const QuantArgs& a, hipStream_t s) {
   if (a.count == 0) return hipSuccess;
-  // 32-position blocks: the range's own, or (per-batch starts) enough blocks
-  // from each start's block to cover count tokens at any alignment
-  const int j0 = a.starts ? 0 : a.start / 32;
-  const int nblk = a.starts ? a.count / 32 + 2 : (a.start + a.count - 1) / 32 - j0 + 1;
+  int j0, nblk;
+  quant_blocks(a, j0, nblk);
   const int64_t n = (int64_t)a.c.B * a.c.H * nblk;
   if (a.c.layout == TAQ_LAYOUT_TOKEN)
     hipLaunchKernelGGL(quantize_token_kernel, dim3((unsigned)n), dim3(a.c.D), 0, s, a, j0, nblk);

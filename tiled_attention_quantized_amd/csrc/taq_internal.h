@@ -77,6 +77,8 @@ struct MaskGenArgs {
 hipError_t launch_tile_mask(const MaskGenArgs& a, hipStream_t s);
 
 hipError_t launch_kv_quantize(const QuantArgs& a, hipStream_t s);
+// Two caches of equal head_dim over the same token range, one launch.
+hipError_t launch_kv_quantize_pair(const QuantArgs& a0, const QuantArgs& a1, hipStream_t s);
 hipError_t launch_head_assign(const uint16_t* o8, const uint16_t* o4, int B, int Hq, int Hkv,
                               int n_high, double* scores, uint8_t* bits, hipStream_t s);
 hipError_t launch_kv_dequantize(const QuantArgs& a, hipStream_t s);
