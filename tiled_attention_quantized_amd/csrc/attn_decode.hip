@@ -45,6 +45,9 @@ namespace {
 
 constexpr int D = 128;
 constexpr int STEP = 32;       // tokens per wave step
+constexpr int MAX_CHUNK = 4096;   // tokens per split chunk, at most
+// a chunk's 128-token KV tiles fit one 32-bit keep mask
+static_assert(MAX_CHUNK / 128 <= 32, "chunk tile mask is 32 bits");
 constexpr int WAVES = 4;
 constexpr float NEG_BIG = -1.0e30f;
 
@@ -518,8 +521,8 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
   const int t_end = min(c0 + a.chunk, n);
   const int t_safe = c0;   // a valid step address (c * chunk < n)
 
-  // KV-tile keep bits of the chunk's tiles (chunk <= 4096: at most 32 tiles of
-  // 128 tokens), read once so that the step loop does no mask loads.
+  // KV-tile keep bits of the chunk's tiles (chunk <= MAX_CHUNK: at most 32
+  // tiles of 128 tokens), read once so that the step loop does no mask loads.
   uint32_t tbits = 0xFFFFFFFFu;
   if (a.mask) {
     const uint8_t* mrow = a.mask + (int64_t)b * a.mask_sb + (int64_t)g * a.mask_sh + (c0 >> 7);
@@ -744,7 +747,7 @@ decode_merge_kernel(DecodeArgs a) {
 int decode_chunk_tokens(int B, int Hkv, int max_len) {
   // Largest chunk (<= 4096 tokens) that still gives >= 2048 workgroups, so
   // every CU gets several; at least 128 (32 tokens per wave).
-  int chunk = 4096;
+  int chunk = MAX_CHUNK;
   const int64_t units = (int64_t)B * Hkv;
   while (chunk > 128 && units * ((max_len + chunk - 1) / chunk) < 2048) chunk /= 2;
   return chunk;
