@@ -71,14 +71,16 @@ def test_decode_with_tile_mask(bits):
     assert not got[2].any()
 
 
-def test_decode_multistep_waves_with_mask():
+@pytest.mark.parametrize("r", [1, 2, 4, 8])
+def test_decode_multistep_waves_with_mask(r):
     """Shapes whose split uses 1024-token chunks (8 steps of 32 tokens per
     wave), so the step pipeline runs with its buffers in rotation: ragged odd
     lengths (a partial last step), a KV-tile mask that drops tiles inside a
-    wave's range (steps skipped mid-range), int8 and int4 heads."""
+    wave's range (steps skipped mid-range), int8 and int4 heads, every GQA
+    ratio (r = 8 carries two row blocks of query heads per lane)."""
     require_gpu()
-    spec = W.small("decode", B=16, Hq=32, Hkv=8, ragged=(9001, 16383), bits=4,
-                   n_int8_heads=2, seed=77, capacity=16384)
+    spec = W.small("decode", B=16, Hq=8 * r, Hkv=8, ragged=(9001, 16383), bits=4,
+                   n_int8_heads=2, seed=77 + r, capacity=16384)
     inp = W.make_inputs(spec)
     kc = T.KVCache(spec.B, spec.Hkv, spec.D, spec.cap, inp.structure.head_bits, T.LAYOUT_TOKEN)
     ws_bytes = T.decode_workspace_bytes(kc, spec.Hq, spec.max_len)
@@ -90,7 +92,7 @@ def test_decode_multistep_waves_with_mask():
     rng = np.random.default_rng(7)
     mask = (rng.random((spec.B, nk)) < 0.7).astype(np.uint8)
     mask[:, 0] = 1
-    note(f"decode multi-step waves, chunk {chunk}, lens {inp.structure.seq_lens.tolist()}")
+    note(f"decode multi-step waves r={r}, chunk {chunk}, lens {inp.structure.seq_lens.tolist()}")
     got, want, _ = run_decode(inp, mask=mask, workers=8)
     err = max_abs(got, want)
     assert err <= TOL, err
