@@ -134,3 +134,22 @@ def test_two_pass_long_context_sampled():
         vh = oq.dequantize(*oq.quantize(inp.v[b, g, :n], int(bits[g])))
         want = oa.decode(inp.q[b:b + 1, h:h + 1], kh[None, None], vh[None, None], [n])[0, 0]
         assert max_abs(two[b, h], want) <= TOL, (b, h)
+
+
+@pytest.mark.parametrize("r", [1, 8])
+def test_two_pass_multistep_waves_with_mask(r):
+    """1024-token split chunks (8 steps per wave) through both passes: ragged
+    odd lengths, tiles dropped inside a wave's range, int8 and int4 heads."""
+    require_gpu()
+    spec = W.small("decode", B=16, Hq=8 * r, Hkv=8, ragged=(9001, 16383), bits=4,
+                   n_int8_heads=2, seed=700 + r, capacity=16384)
+    inp = W.make_inputs(spec)
+    nk = spec.cap // 128
+    rng = np.random.default_rng(11)
+    mask = (rng.random((spec.B, nk)) < 0.7).astype(np.uint8)
+    mask[:, 0] = 1
+    note(f"two-pass multi-step r={r}")
+    two, one, want, _ = _run(inp, mask=mask)
+    assert max_abs(two, want) <= TOL
+    assert max_abs(one, want) <= TOL
+    assert max_abs(two, one) <= TOL
