@@ -318,3 +318,25 @@ def test_head_sensitivity_rejects():
     assert sens_call(ws=0)[0] == WS_SMALL
     if not os.path.exists("/dev/kfd"):
         assert sens_call()[0] == HIP                      # valid: stops at the device query
+
+
+def test_c_consumer_of_the_header(tmp_path):
+    """The header compiles as C99 and a plain C program linked against the
+    library gets the documented sizes and statuses (no GPU needed)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    here = os.path.dirname(os.path.abspath(__file__))
+    src = os.path.join(here, "c_abi", "abi_check.c")
+    libdir = os.path.dirname(T.LIB_PATH)
+    exe = str(tmp_path / "abi_check")
+    hip_lib = "/opt/rocm/lib"
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+           src, "-o", exe, "-L", libdir, "-l:libtaq.so", "-Wl,--allow-shlib-undefined",
+           f"-Wl,-rpath,{libdir}", f"-Wl,-rpath,{hip_lib}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
