@@ -204,3 +204,20 @@ def test_chunk_key_range_split_int4_and_mixed(bits, n8):
                                        n_int8=n8, also_unsplit=True)
         assert max_abs(got, want) <= TOL
         assert max_abs(got, one) <= TOL
+
+
+def test_chunk_zero_length_entry():
+    """An empty batch entry in a chunk over a long history, through the
+    key-range split (its partials carry a zero normaliser into the merge) and
+    without it: its rows are all zero, the live entries match the oracle."""
+    require_gpu()
+    cap, Lq = 2048, 100
+    lens = np.array([2048, 0, 700], dtype=np.int32)
+    kd = T.KVCache(3, 2, 128, cap, [8, 8], T.LAYOUT_TOKEN)
+    assert T.prefill_chunk_workspace_bytes(kd, 8, Lq, cap) > 0     # the split is taken
+    note(f"chunk zero-length entry lens={lens.tolist()}")
+    (got, one), want = _chunk_case(4, Lq, lens, cap, seed=560, bits=4, n_int8=1,
+                                   also_unsplit=True)
+    assert max_abs(got, want) <= TOL
+    assert max_abs(got, one) <= TOL
+    assert not got[1].any() and not one[1].any()

@@ -64,6 +64,25 @@ def test_prefill_small_dense(r, L):
     assert not got[1, :, lens[1]:].any()
 
 
+@pytest.mark.parametrize("r", [1, 4])
+def test_prefill_zero_length_entry(r):
+    """An empty batch entry between two live ones (mixed int4/int8 heads): no
+    key is visible to any of its rows, so they are all zero; the live entries
+    match the oracle."""
+    require_gpu()
+    Hkv = 2
+    spec = W.small("prefill", B=3, Hq=Hkv * r, Hkv=Hkv, L=200, bits=4, n_int8_heads=1,
+                   seed=90 + r)
+    inp = W.make_inputs(spec)
+    lens = np.array([200, 0, 77], dtype=np.int32)
+    note(f"prefill zero-length entry r={r} lens={lens.tolist()}")
+    got, _ = gpu_run_np(inp, lens=lens)
+    want = oracle_run(inp, lens=lens)
+    assert max_abs(got, want) <= TOL
+    assert not got[1].any()
+    assert not got[2, :, 77:].any()
+
+
 @pytest.mark.parametrize("bits,n8", [(4, 0), (4, 1), (8, 1)])
 def test_prefill_bits(bits, n8):
     require_gpu()
