@@ -57,7 +57,11 @@ def test_quantize_bit_exact(layout, lname, bits, D):
     o32, o16 = T.kv_dequantize(gc, 0, cap, f32=True, f16=True)
     want = oq.dequantized_all(oc)
     assert np.array_equal(o32.cpu().numpy().astype(np.float64), want)
-    w16 = want.astype(np.float16)
+    # The fp16 extremes among the adversarial groups dequantise to exact values
+    # beyond fp16's finite range (from 65520 up): RNE gives +-inf there, on both
+    # sides, and the bit patterns still have to match.
+    with np.errstate(over="ignore"):
+        w16 = want.astype(np.float16)
     assert np.array_equal(o16.cpu().numpy().view(np.uint16), w16.view(np.uint16))
 
 
