@@ -1,5 +1,6 @@
 """GPU parity of attn_decode against the fp64 oracle (max-abs <= 2e-3), plus
-edge cases, full-size workloads on sampled heads and run-to-run determinism."""
+edge cases and run-to-run determinism (every output of the full-size
+workloads: test_gpu_full_size.py)."""
 import numpy as np
 import pytest
 import torch
@@ -180,47 +181,6 @@ def test_decode_deterministic():
         torch.cuda.synchronize()
         assert np.array_equal(again.cpu().numpy().view(np.uint16),
                               got.astype(np.float16).view(np.uint16))
-
-
-def test_decode_4k_workload_full():
-    """B=1, Hq=8, Hkv=2, context 4096, int8: every output checked."""
-    require_gpu()
-    inp = W.make_inputs(W.WORKLOADS["decode_4k"])
-    note("decode_4k full")
-    got, want, _ = run_decode(inp)
-    assert max_abs(got, want) <= TOL
-
-
-@pytest.mark.parametrize("name", ["decode_ragged", "decode_128k_mixed"])
-def test_decode_full_size_sampled(name):
-    """Full-size workloads in the benchmarked launch configuration; the oracle
-    checks a sample of (batch, query head) outputs."""
-    require_gpu()
-    spec = W.WORKLOADS[name]
-    inp = W.make_inputs(spec)
-    rng = np.random.default_rng(0)
-    B, Hq = spec.B, spec.Hq
-    heads = sorted({(int(b), int(h)) for b, h in zip(rng.integers(0, B, 12), rng.integers(0, Hq, 12))}
-                   | {(0, 0), (B - 1, Hq - 1)})
-    note(f"{name} full size, sampled heads {heads}")
-    st = inp.structure
-    bits = st.head_bits
-    kc = gpu_cache(inp.k, bits, T.LAYOUT_TOKEN, spec.cap)
-    vc = gpu_cache(inp.v, bits, T.LAYOUT_CHANNEL, spec.cap)
-    q = torch.from_numpy(inp.q).cuda()
-    out = T.attn_decode(kc, vc, q, lens_tensor(st.seq_lens), spec.max_len)
-    torch.cuda.synchronize()
-    got = out.cpu().numpy().astype(np.float64)
-    del kc, vc
-    r = spec.r
-    for b, h in heads:
-        g = h // r
-        n = int(st.seq_lens[b])
-        kh = oq.dequantize(*oq.quantize(inp.k[b, g, :n], int(bits[g])))
-        vh = oq.dequantize(*oq.quantize(inp.v[b, g, :n], int(bits[g])))
-        want = oa.decode(inp.q[b:b + 1, h:h + 1], kh[None, None], vh[None, None], [n])[0, 0]
-        err = max_abs(got[b, h], want)
-        assert err <= TOL, (b, h, err)
 
 
 def test_decode_error_scales_with_v_magnitude():

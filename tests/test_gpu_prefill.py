@@ -1,7 +1,7 @@
 """GPU parity of attn_prefill against the fp64 oracle (max-abs <= 2e-3): small
 shapes checked everywhere (ragged lengths, several tiles and a ragged tail,
-masks, GQA ratios, mixed bits), full-size workloads on sampled rows, invariants
-and determinism."""
+masks, GQA ratios, mixed bits), invariants and determinism (the full-size
+workloads: test_gpu_full_size.py)."""
 import numpy as np
 import pytest
 import torch
@@ -128,38 +128,3 @@ def test_prefill_uniform_v_and_determinism():
         torch.cuda.synchronize()
         assert np.array_equal(again.cpu().numpy().view(np.uint16),
                               got.astype(np.float16).view(np.uint16))
-
-
-def _sample_rows(L, rng, n=48):
-    fixed = [0, 1, 2, 3, 127, 128, 129, L // 2, L - 129, L - 128, L - 2, L - 1]
-    rows = set(int(x) for x in fixed if 0 <= x < L)
-    rows |= set(int(x) for x in rng.integers(0, L, n))
-    return np.array(sorted(rows))
-
-
-@pytest.mark.parametrize("name", ["prefill_8k", "prefill_128k_sparse"])
-def test_prefill_full_size_sampled(name):
-    """Full-size workloads in the benchmarked launch configuration; sampled
-    rows of sampled heads against the oracle."""
-    require_gpu()
-    spec = W.WORKLOADS[name]
-    inp = W.make_inputs(spec)
-    st = inp.structure
-    rng = np.random.default_rng(1)
-    note(f"{name} full size")
-    out, ctx = gpu_run(inp, mask=st.mask)
-    del ctx
-    rows = _sample_rows(spec.context, rng)
-    heads = [(0, 0), (0, 5), (0, 18), (0, 31)]
-    bits = st.head_bits
-    r = spec.r
-    for b, h in heads:
-        g = h // r
-        n = int(st.seq_lens[b])
-        kh = oq.dequantize(*oq.quantize(inp.k[b, g, :n], int(bits[g])))
-        vh = oq.dequantize(*oq.quantize(inp.v[b, g, :n], int(bits[g])))
-        want = oa.prefill(inp.q[b:b + 1, h:h + 1], kh[None, None], vh[None, None], [n],
-                          mask=st.mask, rows=rows)[0, 0]
-        got = out[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
-        err = max_abs(got, want)
-        assert err <= TOL, (h, err)
