@@ -58,7 +58,9 @@
  * - The library allocates no device memory; scratch data goes to caller
  *   workspaces, each sized by its *_workspace_bytes call (decode partials,
  *   chunked-prefill key-range partials, mask-generator sums and scores,
- *   head-sensitivity caches).
+ *   head-sensitivity caches).  The one exception is taq_attn_decode_noalloc,
+ *   for callers that cannot allocate: its scratch is a fixed device array
+ *   that comes with the library (TAQ_DECODE_SCRATCH_BYTES per GPU).
  * - Device pointers must be 16-byte aligned (TAQ_ERR_MISALIGNED otherwise).
  * - Device-resident lengths are clamped to [0, max_seq_len] by the kernels.
  * - softmax_scale = 0 means 1/sqrt(head_dim); negative scales are UNSUPPORTED.
@@ -206,6 +208,31 @@ taq_status taq_attn_decode_two_pass(const taq_kv_cache* k_cache,
                                     int32_t max_seq_len, const taq_tile_mask* mask,
                                     float softmax_scale, void* o_f16, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/* Bytes of the library's own decode scratch array on each GPU (used only by
+ * taq_attn_decode_noalloc). */
+#define TAQ_DECODE_SCRATCH_BYTES (16u * 1024u * 1024u)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * taq_attn_decode without a workspace argument.  The split partials go to a
+ * file-scope device array of TAQ_DECODE_SCRATCH_BYTES bytes that the library
+ * holds on every GPU it runs on until the process ends; the call itself
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * Limit: taq_attn_decode_workspace_bytes() of the call's shapes must not
+ * exceed TAQ_DECODE_SCRATCH_BYTES, else WORKSPACE_TOO_SMALL and nothing is
+ * launched (with Hq = 32 and Hkv = 8, B = 64 at 32K context needs 8.5 MB and
+ * B = 8 at 128K needs 4.3 MB).  Every call on one GPU shares that GPU's array,
+ * which keeps the last call's contents: calls that overlap on one GPU (other
+ * streams, other threads) race and give undefined results, so serialise
+ * them.  No part of the array needs to start at zero.  Results are bitwise
+ * those of taq_attn_decode with the same arguments.  Arguments and other
+ * errors as taq_attn_decode. */
+taq_status taq_attn_decode_noalloc(const taq_kv_cache* k_cache,
+                                   const taq_kv_cache* v_cache, const void* q_f16,
+                                   int32_t num_q_heads, const int32_t* seq_lens,
+                                   int32_t max_seq_len, const taq_tile_mask* mask,
+                                   float softmax_scale, void* o_f16, void* stream);
 
 /* Causal prefill with equal query and key lengths: q/o [B][Hq][L][D] where
  * L = max_seq_len; row i of batch b attends to keys j <= i, j < seq_lens[b],

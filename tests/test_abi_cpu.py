@@ -121,6 +121,15 @@ def decode_two_pass_call(k=None, v=None, hq=8, max_len=200, mask=None, ws_bytes=
                                                       None))
 
 
+def decode_noalloc_call(k=None, v=None, hq=8, max_len=200, mask=None, q=FAKE, o=FAKE,
+                        lens=FAKE, scale=0.0):
+    k = k or cache(B=1, H=2, cap=256, bits=(8, 8), layout=0)
+    v = v or cache(B=1, H=2, cap=256, bits=(8, 8), layout=1)
+    m = ctypes.byref(mask) if mask is not None else None
+    return status_of(T.lib().taq_attn_decode_noalloc(ctypes.byref(k), ctypes.byref(v), q, hq,
+                                                     lens, max_len, m, scale, o, None))
+
+
 def prefill_call(k=None, v=None, hq=8, max_len=200, mask=None, q=FAKE, o=FAKE, lens=FAKE,
                  scale=0.0):
     k = k or cache(B=1, H=2, cap=256, bits=(8, 8), layout=0)
@@ -130,7 +139,8 @@ def prefill_call(k=None, v=None, hq=8, max_len=200, mask=None, q=FAKE, o=FAKE, l
                                               max_len, m, scale, o, None))
 
 
-@pytest.mark.parametrize("call", [decode_call, decode_two_pass_call, prefill_call])
+@pytest.mark.parametrize("call", [decode_call, decode_two_pass_call, decode_noalloc_call,
+                                  prefill_call])
 def test_attention_rejects(call):
     assert call(hq=7)[0] == INVALID                      # Hq % Hkv != 0
     assert call(hq=6)[0] == UNSUPPORTED                  # r = 3
@@ -165,6 +175,25 @@ def test_decode_workspace_too_small():
     assert decode_two_pass_call(ws_bytes=16)[0] == WS_SMALL
 
 
+def test_decode_noalloc_rejects_shapes_beyond_its_scratch():
+    """The allocation-free decode refuses, before touching the device, shapes
+    whose split partials exceed its fixed scratch; shapes that fit get past
+    the check."""
+    k = cache(B=64, H=8, cap=131072, bits=(4,) * 8, layout=0)
+    v = cache(B=64, H=8, cap=131072, bits=(4,) * 8, layout=1)
+    need = T.lib().taq_attn_decode_workspace_bytes(ctypes.byref(k), 64, 131072)
+    assert need > 16 * 1024 * 1024
+    rc, msg = decode_noalloc_call(k=k, v=v, hq=64, max_len=131072)
+    assert rc == WS_SMALL and "scratch" in msg, msg
+    k = cache(B=8, H=8, cap=131072, bits=(4,) * 8, layout=0)
+    v = cache(B=8, H=8, cap=131072, bits=(4,) * 8, layout=1)
+    assert T.lib().taq_attn_decode_workspace_bytes(ctypes.byref(k), 32, 131072) <= 16 << 20
+    if not os.path.exists("/dev/kfd"):
+        # no GPU: shapes that fit get past the check and stop at the device query
+        rc, msg = decode_noalloc_call(k=k, v=v, hq=32, max_len=131072)
+        assert rc == HIP, msg
+
+
 def test_valid_arguments_reach_the_device_check():
     # No GPU in this container: valid arguments get past validation and stop at
     # the device query with a HIP status, never at a fallback.
@@ -173,6 +202,8 @@ def test_valid_arguments_reach_the_device_check():
     rc, msg = decode_call()
     assert rc == HIP, msg
     rc, msg = decode_two_pass_call()
+    assert rc == HIP, msg
+    rc, msg = decode_noalloc_call()
     assert rc == HIP, msg
     rc, msg = prefill_call()
     assert rc == HIP, msg

@@ -34,7 +34,8 @@ EXPORTS = ("taq_last_error", "taq_abi_version", "taq_device_check",
            "taq_kv_append", "taq_attn_prefill_chunk", "taq_tile_mask_workspace_bytes",
            "taq_tile_mask_generate", "taq_attn_decode_two_pass",
            "taq_head_sensitivity_workspace_bytes", "taq_head_sensitivity",
-           "taq_attn_prefill_chunk_workspace_bytes", "taq_kv_quantize_pair")
+           "taq_attn_prefill_chunk_workspace_bytes", "taq_kv_quantize_pair",
+           "taq_attn_decode_noalloc")
 
 
 class TaqError(RuntimeError):
@@ -85,6 +86,7 @@ def lib() -> ctypes.CDLL:
         "taq_attn_decode_workspace_bytes": (SZ, [CP, I32, I32]),
         "taq_attn_decode": (ctypes.c_int, [CP, CP, P, I32, P, I32, MP, F, P, P, SZ, P]),
         "taq_attn_decode_two_pass": (ctypes.c_int, [CP, CP, P, I32, P, I32, MP, F, P, P, SZ, P]),
+        "taq_attn_decode_noalloc": (ctypes.c_int, [CP, CP, P, I32, P, I32, MP, F, P, P]),
         "taq_attn_prefill": (ctypes.c_int, [CP, CP, P, I32, P, I32, MP, F, P, P]),
         "taq_debug_set_arch_override": (None, [ctypes.c_char_p]),
         "taq_kv_append": (ctypes.c_int, [CP, P, P, I32, P]),
@@ -258,6 +260,21 @@ def attn_decode(k: KVCache, v: KVCache, q, seq_lens, max_seq_len: int,
               ctypes.byref(md) if md is not None else None, softmax_scale, _ptr(out),
               _ptr(workspace), workspace.numel() * workspace.element_size(),
               _stream(q.device)))
+    return out
+
+
+def attn_decode_noalloc(k: KVCache, v: KVCache, q, seq_lens, max_seq_len: int, out,
+                        mask: Optional[TileMask] = None, softmax_scale: float = 0.0):
+    """Decode attention with no workspace: the split partials go to the
+    library's own fixed device scratch (TAQ_DECODE_SCRATCH_BYTES per GPU);
+    nothing is allocated, so the caller passes the output tensor."""
+    B, Hq, D = q.shape
+    kd, vd = k.desc(), v.desc()
+    md = mask.desc() if mask is not None else None
+    _check(lib().taq_attn_decode_noalloc(ctypes.byref(kd), ctypes.byref(vd), _ptr(q), Hq,
+                                         _ptr(seq_lens), max_seq_len,
+                                         ctypes.byref(md) if md is not None else None,
+                                         softmax_scale, _ptr(out), _stream(q.device)))
     return out
 
 

@@ -270,11 +270,10 @@ size_t taq_attn_decode_workspace_bytes(const taq_kv_cache* k, int32_t hq, int32_
 
 namespace {
 
-// Shared body of taq_attn_decode (online softmax) and taq_attn_decode_two_pass.
-taq_status decode_common(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
-                         int32_t hq, const int32_t* lens, int32_t max_len,
-                         const taq_tile_mask* mask, float softmax_scale, void* o, void* ws,
-                         size_t ws_bytes, void* stream, bool two_pass) {
+// Host-visible arguments of a decode call other than the workspace.
+taq_status decode_validate(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
+                           int32_t hq, const int32_t* lens, int32_t max_len,
+                           const taq_tile_mask* mask, float softmax_scale, void* o) {
   taq_status st = check_pair(k, v, hq, max_len);
   if (st) return st;
   if (!q || !o || !lens) return fail(TAQ_ERR_INVALID_ARGUMENT, "null q, o or seq_lens");
@@ -284,7 +283,16 @@ taq_status decode_common(const taq_kv_cache* k, const taq_kv_cache* v, const voi
     return fail(TAQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
   if (softmax_scale < 0.f)
     return fail(TAQ_ERR_UNSUPPORTED, "softmax_scale must be >= 0 (0 selects 1/sqrt(head_dim))");
-  st = check_mask(mask, 1, (max_len + TAQ_TILE - 1) / TAQ_TILE);
+  return check_mask(mask, 1, (max_len + TAQ_TILE - 1) / TAQ_TILE);
+}
+
+// Shared body of taq_attn_decode (online softmax), taq_attn_decode_two_pass
+// and taq_attn_decode_noalloc.
+taq_status decode_common(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
+                         int32_t hq, const int32_t* lens, int32_t max_len,
+                         const taq_tile_mask* mask, float softmax_scale, void* o, void* ws,
+                         size_t ws_bytes, void* stream, bool two_pass) {
+  taq_status st = decode_validate(k, v, q, hq, lens, max_len, mask, softmax_scale, o);
   if (st) return st;
   const size_t need = taq_attn_decode_workspace_bytes(k, hq, max_len);
   if (!ws || ws_bytes < need)
@@ -336,6 +344,70 @@ taq_status taq_attn_decode_two_pass(const taq_kv_cache* k, const taq_kv_cache* v
                                     void* stream) {
   return decode_common(k, v, q, hq, lens, max_len, mask, softmax_scale, o, ws, ws_bytes, stream,
                        true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of taq_attn_decode_noalloc: the decode split partials, in a
+// file-scope device array that every GPU the library runs on holds until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device memory: its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever handed to a kernel.  Nothing in it has to start
+// at zero (each call writes every partial it reads), and calls that overlap
+// on one GPU share it and race.
+static __device__ __align__(256) unsigned char scratch[TAQ_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on each device).
+taq_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(TAQ_ERR_UNSUPPORTED, "device %d: the no-allocation scratch covers devices 0..%d",
+                dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(TAQ_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return TAQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+taq_status taq_attn_decode_noalloc(const taq_kv_cache* k, const taq_kv_cache* v, const void* q,
+                                   int32_t hq, const int32_t* lens, int32_t max_len,
+                                   const taq_tile_mask* mask, float softmax_scale, void* o,
+                                   void* stream) {
+  taq_status st = decode_validate(k, v, q, hq, lens, max_len, mask, softmax_scale, o);
+  if (st) return st;
+  const size_t need = taq_attn_decode_workspace_bytes(k, hq, max_len);
+  if (need > (size_t)TAQ_DECODE_SCRATCH_BYTES)
+    return fail(TAQ_ERR_WORKSPACE_TOO_SMALL,
+                "these shapes need %zu bytes of decode scratch; the no-allocation decode holds "
+                "%zu (use taq_attn_decode with a workspace)", need,
+                (size_t)TAQ_DECODE_SCRATCH_BYTES);
+  st = device_ok();
+  if (st) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st) return st;
+  return decode_common(k, v, q, hq, lens, max_len, mask, softmax_scale, o, ws,
+                       (size_t)TAQ_DECODE_SCRATCH_BYTES, stream, false);
 }
 
 }  // extern "C"
