@@ -9,19 +9,36 @@
 // 2.3; prefill is compute-bound and skips aggressively, section 5.3).
 //
 // Work decomposition (gfx950):
-//  * a 512-thread workgroup (8 waves) owns BQ = 256 / r query rows of all
-//    r = Hq/Hkv query heads that share one KV head, so every K/V tile is
-//    fetched and dequantised once for r * BQ = 256 (head, row) pairs; wave w
+//  * a 512-thread workgroup (8 waves, two per SIMD: the second wave of a SIMD
+//    issues while the first waits on a matrix instruction) owns BQ = 256 / r
+//    query rows of all r = Hq/Hkv query heads that share one KV head, so every
+//    K/V tile is fetched and dequantised once for 256 (head, row) pairs; wave w
 //    takes head w % r and the 32 rows (w / r) * 32 .. +31;
-//  * the key loop runs in tiles of 64 keys through three LDS stages as a
-//    software pipeline: the QK^T MFMAs of tile j+1 interleave with the
-//    softmax of tile j, and the PV MFMAs of tile j with the dequantisation of
-//    tile j+2; tile j+3 is fetched into registers (one barrier per tile);
+//  * the key loop runs over the workgroup's needed 64-key tiles through three
+//    LDS stages as a software pipeline with one barrier per tile: the QK^T
+//    MFMAs of tile j+1 interleave with the weights of tile j, and the PV MFMAs
+//    of tile j with the dequantisation of tile j+2; tile j+3 is fetched into
+//    registers.  Inside those blocks each chain of dependent vector
+//    instructions (exponent argument, exponential, fp16 rounding and row sum;
+//    codes to fp16, zero-point, scale) is spread over three matrix-instruction
+//    slices, so no instruction waits on the one just before it;
 //  * both contractions use v_mfma_f32_32x32x16_f16 in transposed form:
 //    S^T = K-hat Q^T (A = K-hat tile from LDS, B = Q held in registers) and
 //    O^T += V-hat^T P^T (A = V-hat^T tile from LDS, B = P straight from the
 //    S^T accumulator), so every lane owns one query row for the whole loop and
-//    the softmax needs only one cross-lane exchange per tile;
+//    the softmax statistics stay lane-local;
+//  * the running maximum m of a row is not recomputed per tile: the weights
+//    exp2(s - m) of a tile are formed against the current m and rounded to
+//    fp16, and only when a lane's sum of them exceeds 2^15 (a score more than
+//    ~15 above m, or the row's first tile, whose m starts at -1e30) is the
+//    tile's row maximum taken, m moved, the accumulator and normaliser
+//    rescaled and the weights recomputed (a rare branch).  The result is the
+//    same softmax: the factor exp2(-m) cancels between numerator and
+//    normaliser;
+//  * the needed tiles are found from scalar bit windows over 32 mask tiles
+//    (one vector load and ballot per window and query tile), and the
+//    causal / length / mask masking of a tile's scores only runs on tiles
+//    that need it;
 //  * the workgroup order runs the longest causal rows first.
 #include "taq_internal.h"
 #include "device_common.h"
@@ -33,20 +50,20 @@ constexpr int D = 128;
 constexpr int KT = 64;                 // keys per tile
 constexpr int NWAVE = 8;
 constexpr int NT = 64 * NWAVE;
+constexpr int NBLK = 8;                // 32-row blocks per workgroup (one per wave)
 constexpr int KS_STRIDE = D * 2 + 16;  // bytes per K-hat row in LDS (padded)
 constexpr int VS_STRIDE = KT * 2 + 16; // bytes per V-hat^T row in LDS (padded)
 constexpr int LDS_K = KT * KS_STRIDE;
 constexpr int LDS_V = D * VS_STRIDE;
 constexpr int LDS_STAGE = LDS_K + LDS_V;   // one tile (K-hat and V-hat^T)
+constexpr int NSTAGE = 3;
 constexpr float NEG_BIG = -1.0e30f;
+// A lane's weights of one tile are safe in fp16 (and exact enough) while
+// their sum stays at or below this; above it the tile takes the rescale path.
+constexpr float P_SUM_LIMIT = 32768.f;
 // key-range partial of one (split, b, query head, row): m, l, 2 pad, acc[D]
 // (16-byte aligned records)
 constexpr int PART_REC = D + 4;
-#ifndef TAQ_PREFILL_READ_AHEAD
-#define TAQ_PREFILL_READ_AHEAD 3
-#endif
-// LDS operand reads issued this many matrix instructions ahead of their use.
-constexpr int PF_RA = TAQ_PREFILL_READ_AHEAD;
 
 // V-hat^T rows hold the keys of each 16-key group in the order that the PV
 // operand wants them: key 16g + 8a + 4h + c (a, h in {0,1}, c in 0..3) sits at
@@ -63,139 +80,98 @@ __device__ __forceinline__ uint32_t nib_pair_natural(uint32_t w, int j) {
 }
 
 // Registers holding one tile's raw codes and metadata for this thread.
+// K: thread (key = tid / 8, group = (tid / 2) % 4, half = tid % 2), 16
+// channels of one key.  V: thread (channel d = tid / 4, quarter q = tid % 4),
+// keys 16 q .. 16 q + 15 of the tile.
 struct Staged {
-  u32x4 kc;        // K codes: 16 channels (int8: 16 B; int4: first 8 B used)
+  u32x4 kc;        // K codes (int8: 16 B; int4: first 8 B)
   uint32_t kz;     // K zero byte
   uint32_t ks;     // K scale bits
-  u32x4 vc;        // V codes: 16 keys of one channel
-  u32x4 vz;        // V zeros of those 16 keys
-  u32x4 vs0, vs1;  // V scales of those 16 keys
+  u32x4 vc;        // V codes (int8: 16 B; int4: first 8 B)
+  u32x4 vz;        // V zeros of the 16 keys
+  u32x4 vs[2];     // V scales of the 16 keys
 };
 
-// Tile-invariant addressing: uniform (scalar) base pointers of this (batch,
-// KV head) and the per-thread offsets of its share of a tile, so a tile load
-// is a scalar base plus a fixed 32-bit lane offset.
-struct TileCtx {
-  const uint8_t* kbase;
-  const uint8_t* vbase;
-  const uint16_t* kscale;
-  const uint8_t* kzero;
-  const uint16_t* vscale;
-  const uint8_t* vzero;
-  uint32_t k_off;     // K codes, bytes from the tile's first key row
-  uint32_t km_off;    // K scale / zero index from the tile's first key
-  uint32_t v_off;     // V codes, bytes from the tile's first 32-key block
-  uint32_t vm_off;    // V scale / zero index from the tile's first key
+// Base addresses of one (batch, KV head) slab.  A tile load is a uniform
+// base (held in scalar registers) plus a uniform tile offset plus a fixed
+// 32-bit per-lane offset.  Every tile a workgroup loads lies below the
+// sequence length, so all loads stay inside the slab.
+struct Bases {
+  const uint8_t* k;
+  const uint8_t* kz;
+  const uint8_t* ks;
+  const uint8_t* v;
+  const uint8_t* vz;
+  const uint8_t* vs;
 };
 
-// Staging threads: K -> (key = unit / 4, group = unit % 4, half) with unit =
-// tid / 2, 16 channels each; V -> (channel d = tid / 4, quarter q = tid % 4),
-// keys 16q .. 16q+15 of the tile.
+template <typename T>
+__device__ __forceinline__ T load_at(const uint8_t* base, uint32_t tile_off, uint32_t lane_off) {
+  return *reinterpret_cast<const T*>(base + tile_off + lane_off);
+}
+
+// Per-thread byte offsets of its share of a tile (from the tile's first key).
+struct LaneOff {
+  uint32_t k, km, v, vm;
+};
+
 template <bool K8, bool V8>
-__device__ __forceinline__ void tile_ctx_offsets(TileCtx& c, int tid, int cap) {
+__device__ __forceinline__ LaneOff lane_offsets(int tid, int cap) {
+  LaneOff o;
   const int unit = tid >> 1, half = tid & 1;
-  const int kkey = unit >> 2, kgrp = unit & 3;
-  c.k_off = (uint32_t)(kkey * (K8 ? D : D / 2) + (K8 ? 32 : 16) * kgrp + (K8 ? 16 : 8) * half);
-  c.km_off = (uint32_t)(kkey * 4 + kgrp);
+  const int key = unit >> 2, grp = unit & 3;
+  o.k = (uint32_t)(key * (K8 ? D : D / 2) + (K8 ? 32 : 16) * grp + (K8 ? 16 : 8) * half);
+  o.km = (uint32_t)(key * 4 + grp);
   const int d = tid >> 2, q = tid & 3;
-  const int rowb = V8 ? 32 : 16;
-  // key 16q of the tile lies in 32-key block q / 2 at position 16 (q % 2)
-  c.v_off = (uint32_t)(((q >> 1) * D + d) * rowb + (V8 ? 16 : 8) * (q & 1));
-  c.vm_off = (uint32_t)((d >> 5) * cap + 16 * q);
+  // key 16 q of the tile lies in 32-key block q / 2 at position 16 (q % 2)
+  o.v = (uint32_t)(((q >> 1) * D + d) * (V8 ? 32 : 16) + (V8 ? 16 : 8) * (q & 1));
+  o.vm = (uint32_t)((d >> 5) * cap + 16 * q);
+  return o;
 }
 
 template <bool K8, bool V8>
-__device__ __forceinline__ void stage_load(const TileCtx& c, int kt0, Staged& s) {
-  {
-    const uint8_t* kb = c.kbase + (int64_t)kt0 * (K8 ? D : D / 2);
-    if (K8) {
-      s.kc = *reinterpret_cast<const u32x4*>(kb + c.k_off);
-    } else {
-      const u32x2 t = *reinterpret_cast<const u32x2*>(kb + c.k_off);
-      s.kc = u32x4{t[0], t[1], 0u, 0u};
-    }
-    s.kz = (c.kzero + (int64_t)kt0 * 4)[c.km_off];
-    s.ks = (c.kscale + (int64_t)kt0 * 4)[c.km_off];
+__device__ __forceinline__ void stage_load(const Bases& r, const LaneOff& o, int kt0, Staged& s) {
+  const uint32_t tk = (uint32_t)kt0 * (K8 ? D : D / 2);
+  if (K8) {
+    s.kc = load_at<u32x4>(r.k, tk, o.k);
+  } else {
+    const u32x2 t = load_at<u32x2>(r.k, tk, o.k);
+    s.kc = u32x4{t[0], t[1], 0u, 0u};
   }
-  {
-    const uint8_t* vb = c.vbase + (int64_t)(kt0 >> 5) * D * (V8 ? 32 : 16);
-    if (V8) {
-      s.vc = *reinterpret_cast<const u32x4*>(vb + c.v_off);
-    } else {
-      const u32x2 t = *reinterpret_cast<const u32x2*>(vb + c.v_off);
-      s.vc = u32x4{t[0], t[1], 0u, 0u};
-    }
-    s.vz = *reinterpret_cast<const u32x4*>(c.vzero + kt0 + c.vm_off);
-    const u32x4* sp = reinterpret_cast<const u32x4*>(c.vscale + kt0 + c.vm_off);
-    s.vs0 = sp[0];
-    s.vs1 = sp[1];
+  s.kz = load_at<uint8_t>(r.kz, (uint32_t)kt0 * 4, o.km);
+  s.ks = load_at<uint16_t>(r.ks, (uint32_t)kt0 * 8, 2 * o.km);
+  const uint32_t tv = (uint32_t)(kt0 >> 5) * D * (V8 ? 32 : 16);
+  if (V8) {
+    s.vc = load_at<u32x4>(r.v, tv, o.v);
+  } else {
+    const u32x2 t = load_at<u32x2>(r.v, tv, o.v);
+    s.vc = u32x4{t[0], t[1], 0u, 0u};
   }
+  s.vz = load_at<u32x4>(r.vz, (uint32_t)kt0, o.vm);
+  s.vs[0] = load_at<u32x4>(r.vs, 2 * (uint32_t)kt0, 2 * o.vm);
+  s.vs[1] = load_at<u32x4>(r.vs, 2 * (uint32_t)kt0, 2 * o.vm + 16);
 }
 
-// Dequantise the staged registers into LDS.  Keys at or beyond n get a zero
-// scale so that their (never used) V-hat entries are exactly 0 and finite.
-template <bool K8, bool V8>
-__device__ __forceinline__ void stage_store(const Staged& s, int kt0, int n, int tid,
-                                            char* lds) {
-  {
-    const int unit = tid >> 1, half = tid & 1;
-    const int key = unit >> 2, grp = unit & 3;
-    const half2v nz = u32_to_h2(neg_biased_zero_h2(s.kz));
-    const _Float16 sc = bits_to_half((uint16_t)s.ks);
-    const half2v s2 = half2v{sc, sc};
-    u32x4 o0, o1;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t c2;
-      if (K8) c2 = bytes_to_biased_h2(s.kc[j >> 1], j & 1);
-      else c2 = nib_pair_natural(s.kc[j >> 2], j & 3);
-      const uint32_t v = h2_to_u32((u32_to_h2(c2) + nz) * s2);
-      if (j < 4) o0[j] = v; else o1[j - 4] = v;
-    }
-    u32x4* dst = reinterpret_cast<u32x4*>(lds + key * KS_STRIDE + (32 * grp + 16 * half) * 2);
-    dst[0] = o0;
-    dst[1] = o1;
-  }
-  {
-    const int d = tid >> 2, q = tid & 3;
-    u32x4 o0, o1;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {  // pair j = keys 16q + 2j, +1
-      uint32_t c2;
-      if (V8) c2 = bytes_to_biased_h2(s.vc[j >> 1], j & 1);
-      else c2 = nib_pair_natural(s.vc[j >> 2], j & 3);
-      const uint32_t nz = perm_b32(0xE4E4E4E4u, s.vz[j >> 1], (j & 1) ? 0x04030402u : 0x04010400u);
-      uint32_t sc = j < 4 ? s.vs0[j] : s.vs1[j - 4];
-      const int k0 = kt0 + 16 * q + 2 * j;
-      if (k0 >= n) sc &= 0xFFFF0000u;
-      if (k0 + 1 >= n) sc &= 0x0000FFFFu;
-      const uint32_t v = h2_to_u32((u32_to_h2(c2) + u32_to_h2(nz)) * u32_to_h2(sc));
-      if (vslot(j) < 4) o0[vslot(j)] = v; else o1[vslot(j) - 4] = v;
-    }
-    u32x4* dst = reinterpret_cast<u32x4*>(lds + LDS_K + d * VS_STRIDE + 32 * q);
-    dst[0] = o0;
-    dst[1] = o1;
-  }
-}
-
-// The same dequantisation as stage_store, one fp16 pair at a time and split
-// in two steps (code minus zero point, then times the scale) so that the
-// steps of consecutive pairs can be interleaved with matrix instructions.
-// K: pair j (0..7) = channels 16*half + 2j, +1 of the thread's (key, group);
-// V: pair j = keys 16q + 2j, +1 of the thread's channel.
+// Dequantisation steps of one fp16 pair (K pair j in 0..7 = channels
+// 16 half + 2j, +1 of the thread's (key, group); V pair j = keys 16 q + 2j, +1
+// of the thread's channel): codes to biased fp16 (1024 + c, or the nibble
+// forms), minus the biased zero-point, times the scale.
 template <bool K8>
-__device__ __forceinline__ uint32_t k_centered(const Staged& s, int j, half2v nz) {
-  const uint32_t c2 = K8 ? bytes_to_biased_h2(s.kc[j >> 1], j & 1) : nib_pair_natural(s.kc[j >> 2], j & 3);
-  return h2_to_u32(u32_to_h2(c2) + nz);
+__device__ __forceinline__ uint32_t k_biased(const Staged& s, int j) {
+  return K8 ? bytes_to_biased_h2(s.kc[j >> 1], j & 1) : nib_pair_natural(s.kc[j >> 2], j & 3);
 }
 template <bool V8>
-__device__ __forceinline__ uint32_t v_centered(const Staged& s, int j) {
-  const uint32_t c2 = V8 ? bytes_to_biased_h2(s.vc[j >> 1], j & 1) : nib_pair_natural(s.vc[j >> 2], j & 3);
-  const uint32_t nz = perm_b32(vconst(0xE4E4E4E4u), s.vz[j >> 1], (j & 1) ? 0x04030402u : 0x04010400u);
-  return h2_to_u32(u32_to_h2(c2) + u32_to_h2(nz));
+__device__ __forceinline__ uint32_t v_biased(const Staged& s, int j) {
+  return V8 ? bytes_to_biased_h2(s.vc[j >> 1], j & 1) : nib_pair_natural(s.vc[j >> 2], j & 3);
+}
+__device__ __forceinline__ uint32_t v_negzero(const Staged& s, int j) {
+  return perm_b32(vconst(0xE4E4E4E4u), s.vz[j >> 1], (j & 1) ? 0x04030402u : 0x04010400u);
 }
 __device__ __forceinline__ uint32_t v_scales(const Staged& s, int j) {
-  return j < 4 ? s.vs0[j] : s.vs1[j - 4];
+  return s.vs[j >> 2][j & 3];
+}
+__device__ __forceinline__ uint32_t h2_add(uint32_t a, uint32_t b) {
+  return h2_to_u32(u32_to_h2(a) + u32_to_h2(b));
 }
 __device__ __forceinline__ uint32_t h2_mul(uint32_t a, uint32_t b) {
   return h2_to_u32(u32_to_h2(a) * u32_to_h2(b));
@@ -209,26 +185,56 @@ __device__ __forceinline__ void zero_tail_scales(Staged& s, int key0, int n) {
   for (int j = 0; j < 8; ++j) {
     const int k0 = key0 + 2 * j;
     const uint32_t keep = (k0 < n ? 0x0000FFFFu : 0u) | (k0 + 1 < n ? 0xFFFF0000u : 0u);
-    if (j < 4) s.vs0[j] &= keep; else s.vs1[j - 4] &= keep;
+    s.vs[j >> 2][j & 3] &= keep;
   }
 }
 
-__device__ __forceinline__ bool mask_keep(const PrefillArgs& a, const uint8_t* mb, int qt, int kt) {
-  return mb == nullptr || mb[(int64_t)qt * a.mask_nk + kt] != 0;
+// Dequantise the staged registers into LDS stage `dst` in one go (prologue).
+template <bool K8, bool V8>
+__device__ __forceinline__ void stage_store(const Staged& s, int tid, char* dst) {
+  const uint32_t knz = neg_biased_zero_h2(s.kz);
+  const _Float16 ksc = bits_to_half((uint16_t)s.ks);
+  const uint32_t ks2 = h2_to_u32(half2v{ksc, ksc});
+  const int unit = tid >> 1, half = tid & 1;
+  const int key = unit >> 2, grp = unit & 3;
+  u32x4 ko[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ko[j >> 2][j & 3] = h2_mul(h2_add(k_biased<K8>(s, j), knz), ks2);
+  u32x4* kd = reinterpret_cast<u32x4*>(dst + key * KS_STRIDE + (32 * grp + 16 * half) * 2);
+  kd[0] = ko[0];
+  kd[1] = ko[1];
+  const int d = tid >> 2, q = tid & 3;
+  u32x4 vo[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    vo[vslot(j) >> 2][vslot(j) & 3] = h2_mul(h2_add(v_biased<V8>(s, j), v_negzero(s, j)),
+                                             v_scales(s, j));
+  u32x4* vd = reinterpret_cast<u32x4*>(dst + LDS_K + d * VS_STRIDE + 32 * q);
+  vd[0] = vo[0];
+  vd[1] = vo[1];
+}
+
+// Keep bits of the 32 mask tiles w0 .. w0+31 for query tile qt: bit i set
+// when tile w0 + i lies at or below the diagonal (w0 + i <= qt) and the mask
+// keeps it (every such tile when there is no mask).  One byte load per lane.
+__device__ __forceinline__ uint32_t keep_window(const uint8_t* mrow, int qt, int w0, int lane) {
+  const int kt = w0 + (lane & 31);
+  bool keep = lane < 32 && kt <= qt;
+  if (mrow != nullptr && keep) keep = mrow[kt] != 0;
+  return (uint32_t)__builtin_amdgcn_ballot_w64(keep);
 }
 
 template <int R, bool K8, bool V8>
 __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int split, int n,
                              char* lds) {
-  constexpr int BQ = 32 * (NWAVE / R);
+  constexpr int BQ = 32 * (NBLK / R);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int i32 = lane & 31, hb = lane >> 5;
-  const int hl = w % R, rblk = w / R;
-  const int hq = g * R + hl;
+  const int hq = g * R + w % R;
   const int q0 = qblk * BQ;
-  const int q0w = q0 + 32 * rblk;
+  const int q0w = q0 + 32 * (w / R);
   const int row = q0w + i32;             // row of q / o
   // Position of row 0 in the sequence: 0 for a whole-sequence prefill; for a
   // chunk of Lq new rows whose keys are already in the cache, n - Lq (rows
@@ -238,19 +244,21 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
   const int pos = row + qoff;
   const int p0w = q0w + qoff;            // position of the wave's first row
   const bool row_live = row < a.Lq && pos >= 0 && pos < n;
+  // some row of the wave is padding (masked on every tile)
+  const bool blk_dead = p0w < 0 || p0w + 31 >= n || q0w + 31 >= a.Lq;
 
-  TileCtx c;
-  c.kbase = a.k.codes + (int64_t)b * a.k.bstride + a.k.hoff[g];
-  c.vbase = a.v.codes + (int64_t)b * a.v.bstride + a.v.hoff[g];
-  c.kscale = a.k.scales + ((int64_t)b * a.k.H + g) * a.k.cap * 4;
-  c.kzero = a.k.zeros + ((int64_t)b * a.k.H + g) * a.k.cap * 4;
-  c.vscale = a.v.scales + ((int64_t)b * a.v.H + g) * 4 * (int64_t)a.v.cap;
-  c.vzero = a.v.zeros + ((int64_t)b * a.v.H + g) * 4 * (int64_t)a.v.cap;
-  tile_ctx_offsets<K8, V8>(c, tid, a.k.cap);
+  Bases rs;
+  rs.k = a.k.codes + (int64_t)b * a.k.bstride + a.k.hoff[g];
+  rs.v = a.v.codes + (int64_t)b * a.v.bstride + a.v.hoff[g];
+  rs.ks = reinterpret_cast<const uint8_t*>(a.k.scales + ((int64_t)b * a.k.H + g) * a.k.cap * 4);
+  rs.kz = a.k.zeros + ((int64_t)b * a.k.H + g) * a.k.cap * 4;
+  rs.vs = reinterpret_cast<const uint8_t*>(a.v.scales + ((int64_t)b * a.v.H + g) * 4 * (int64_t)a.v.cap);
+  rs.vz = a.v.zeros + ((int64_t)b * a.v.H + g) * 4 * (int64_t)a.v.cap;
+  const LaneOff lo = lane_offsets<K8, V8>(tid, a.k.cap);
 
   const uint8_t* mb = a.mask ? a.mask + (int64_t)b * a.mask_sb + (int64_t)g * a.mask_sh : nullptr;
 
-  // Q row of this lane (B operand of S^T): channels 16ks + 8hb .. +7
+  // Q row of this lane (B operand of S^T): channels 16 ks + 8 hb .. +7
   half8 qreg[8];
   {
     const uint16_t* qp = a.q + (((int64_t)b * a.Hq + hq) * a.Lq + row) * D + 8 * hb;
@@ -262,8 +270,7 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
     }
   }
 
-  // rows of the workgroup that can see any key, and key range
-  // last live position of the workgroup
+  // key range of the workgroup: up to its last live position
   const int wg_last = min(min(q0 + BQ, a.Lq) - 1 + qoff, n - 1);
   const int nkt_all = wg_last >= 0 ? wg_last / KT + 1 : 0;
   // key-range split: this workgroup takes tiles [kt_lo, nkt) of the query
@@ -271,19 +278,63 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
   const int per = (nkt_all + a.nsplit - 1) / a.nsplit;
   const int kt_lo = min(split * per, nkt_all);
   const int nkt = min(kt_lo + per, nkt_all);
-  const int qt_first = max(q0 + qoff, 0) >> 7, qt_last = wg_last >= 0 ? (wg_last >> 7) : -1;
+  // query tiles of the workgroup's live positions (at most 3)
+  const int qt_first = max(q0 + qoff, 0) >> 7;
+  const int qt_last = wg_last >= 0 ? (wg_last >> 7) : -1;
+  const int nqt = min(qt_last - qt_first + 1, 3);
 
-  auto wg_needs = [&](int kt) -> bool {
-    const int kt128 = (kt * KT) >> 7;
-    for (int qt = qt_first; qt <= qt_last; ++qt)
-      if (qt >= kt128 && mask_keep(a, mb, qt, kt128)) return true;
-    return false;
+  // ---- tile walk over scalar keep windows ----------------------------------
+  // win[i]: keep bits of query tile qt_first + i over mask tiles w0 .. w0+31;
+  // wgwin: their union (the tiles the workgroup needs).
+  int w0 = -32;
+  uint32_t win[3] = {0u, 0u, 0u};
+  uint32_t wgwin = 0u;
+  auto refill = [&](int base) {
+    w0 = base;
+    wgwin = 0u;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      win[i] = 0u;
+      if (i < nqt) {
+        const int qt = qt_first + i;
+        win[i] = keep_window(mb ? mb + (int64_t)qt * a.mask_nk : nullptr, qt, base, lane);
+        wgwin |= win[i];
+      }
+    }
   };
-  auto next_tile = [&](int kt) -> int {
-    if (mb == nullptr) return kt;   // dense: every tile below nkt is needed
-    while (kt < nkt && !wg_needs(kt)) ++kt;
-    return kt;
+  // First needed 64-key tile at or after t (nkt if none), and its keep bits:
+  // bit i of kq set when query tile qt_first + i keeps it.  The bits travel
+  // with the tile (the window may move on before the tile is processed).
+  auto next_tile = [&](int t, uint32_t& kq) -> int {
+    kq = 7u;
+    if (mb == nullptr) return min(t, nkt);   // dense: every tile below nkt is needed
+    while (t < nkt) {
+      const int t128 = t >> 1;
+      if (t128 >= w0 + 32 || t128 < w0) refill(t128 & ~31);
+      const int sh = t128 - w0;
+      const uint32_t bits = wgwin >> sh;
+      if (bits & 1u) {
+        kq = ((win[0] >> sh) & 1u) | (((win[1] >> sh) & 1u) << 1) | (((win[2] >> sh) & 1u) << 2);
+        return t;
+      }
+      if (bits == 0u) {
+        t = 2 * (w0 + 32);
+      } else {
+        t = 2 * (t128 + __builtin_ctz(bits));
+      }
+    }
+    return nkt;
   };
+  // query-tile indices (relative to qt_first) of the wave's first and last
+  // row, and of this lane's row
+  int qia, qib, qil;
+  {
+    const int qa = max(p0w, 0) >> 7, qb = max(min(p0w + 31, n - 1), 0) >> 7;
+    qia = min(max(qa - qt_first, 0), 2);
+    qib = min(max(qb - qt_first, 0), 2);
+    const int ql = max(min(pos, n - 1), 0) >> 7;
+    qil = min(max(ql - qt_first, 0), 2);
+  }
 
   float m_run = NEG_BIG, l_run = 0.f;
   f32x16 o[4];
@@ -293,19 +344,14 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
     for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
 
   const float c_log2 = a.scale_log2;   // > 0 (checked on the host)
-  // this lane's 128-row query tile (clamped, so lanes past the last row never
-  // index beyond the mask's ceil(max_seq_len / 128) tile rows)
-  const int qt_l = min(max(pos, 0), a.L - 1) >> 7;
 
-  // ---- LDS stage helpers ---------------------------------------------------------
-  auto stage_ptr = [&](int j) -> char* { return lds + (j % 3) * LDS_STAGE; };
-  // ring stage after / before stage x (x in 0..2)
+  auto stage_at = [&](int x) -> char* { return lds + x * LDS_STAGE; };
   auto ring_next = [](int x) { return x == 2 ? 0 : x + 1; };
   auto ring_prev = [](int x) { return x == 0 ? 2 : x - 1; };
-  auto stage_at = [&](int x) -> char* { return lds + x * LDS_STAGE; };
-  // S^T = K-hat Q^T for the tile in stage j (16 MFMAs)
-  auto qk = [&](int j, f32x16* S) {
-    const uint8_t* kl = reinterpret_cast<const uint8_t*>(stage_ptr(j));
+
+  // S^T = K-hat Q^T for the tile in stage x (16 MFMAs), no interleaving
+  auto qk_plain = [&](int x, f32x16* S) {
+    const uint8_t* kl = reinterpret_cast<const uint8_t*>(stage_at(x));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -318,13 +364,15 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
       }
     }
   };
-  // causal / length / dead-row / per-wave mask of tile kt on S (only when needed)
-  auto mask_tile = [&](int kt, f32x16* S) {
-    const int kt0 = kt * KT;
-    const bool keep = mask_keep(a, mb, qt_l, kt0 >> 7);
-    const bool need = __any(!keep) || (kt0 + KT - 1 > p0w) || (kt0 + KT > n) || (p0w + 31 >= n) ||
-                      (p0w < 0) || (q0w + 31 >= a.Lq);
+
+  // causal / length / dead-row / mask masking of tile t's scores (keep bits
+  // kq; only on tiles that need it)
+  auto mask_tile = [&](int t, uint32_t kq, f32x16* S) {
+    const int kt0 = t * KT;
+    const bool all_keep = ((kq >> qia) & (kq >> qib) & 1u) != 0u;
+    const bool need = (kt0 + KT - 1 > p0w) || (kt0 + KT > n) || blk_dead || !all_keep;
     if (need) {
+      const bool keep = ((kq >> qil) & 1u) != 0u;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -335,58 +383,74 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
     }
   };
 
+  // Rare path: the tile's row maximum (both lane halves of the row), m moved
+  // to it if larger, accumulator and normaliser rescaled, weights recomputed
+  // into pk; returns the lane's row sum of the new fp16 weights.
+  auto rescale = [&](const f32x16* S, half8 (&pk)[4]) -> float {
+    float mx = S[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kb][v]);
+    mx = fmaxf(mx, lane_read_f(mx, lane ^ 32)) * c_log2;
+    const float mn = fmaxf(m_run, mx);     // rows with no key keep NEG_BIG
+    const float alpha = fast_exp2(m_run - mn);
+    m_run = mn;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db] = o[db] * alpha;
+    const half2v ones = half2v{(_Float16)1.f, (_Float16)1.f};
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const float e0 = fast_exp2(fmaf(S[kb][v], c_log2, -mn));
+        const float e1 = fast_exp2(fmaf(S[kb][v + 1], c_log2, -mn));
+        const half2v hp = half2v{(_Float16)e0, (_Float16)e1};
+        pk[2 * kb + (v >> 3)][v & 7] = hp[0];
+        pk[2 * kb + (v >> 3)][(v & 7) + 1] = hp[1];
+        ls = __builtin_amdgcn_fdot2(hp, ones, ls, false);
+      }
+    return ls;
+  };
+
   // ---- software pipeline over the workgroup's KV tiles -------------------------
   // Tiles t_0, t_1, ... (causal and mask order) go through three LDS stages.
   // Iteration j (one barrier): the QK^T MFMAs of tile j+1 run interleaved with
-  // the softmax of tile j, then the PV MFMAs of tile j run interleaved with the
+  // the weights of tile j, then the PV MFMAs of tile j run interleaved with the
   // dequantisation of tile j+2 into the third stage; tile j+3 is fetched from
   // HBM into registers.  Every wave walks the same tiles; rows a tile does not
   // reach are masked, so the loop has no per-wave branches.
-  const int t0_ = next_tile(kt_lo);
+  uint32_t kq0, kq1 = 7u, kq2 = 7u;
+  const int t0_ = next_tile(kt_lo, kq0);
   if (t0_ < nkt) {
-    const int t1_ = next_tile(t0_ + 1);
-    const int t2_ = t1_ < nkt ? next_tile(t1_ + 1) : nkt;
+    const int t1_ = next_tile(t0_ + 1, kq1);
+    const int t2_ = t1_ < nkt ? next_tile(t1_ + 1, kq2) : nkt;
     Staged st;
-    stage_load<K8, V8>(c, t0_ * KT, st);
-    stage_store<K8, V8>(st, t0_ * KT, n, tid, stage_ptr(0));
-    stage_load<K8, V8>(c, (t1_ < nkt ? t1_ : t0_) * KT, st);
-    stage_store<K8, V8>(st, (t1_ < nkt ? t1_ : t0_) * KT, n, tid, stage_ptr(1));
-    stage_load<K8, V8>(c, (t2_ < nkt ? t2_ : t0_) * KT, st);
+    stage_load<K8, V8>(rs, lo, t0_ * KT, st);
+    if (t0_ * KT + KT > n) zero_tail_scales(st, t0_ * KT + 16 * (tid & 3), n);
+    stage_store<K8, V8>(st, tid, stage_at(0));
+    const int ta = t1_ < nkt ? t1_ : t0_;
+    stage_load<K8, V8>(rs, lo, ta * KT, st);
+    if (ta * KT + KT > n) zero_tail_scales(st, ta * KT + 16 * (tid & 3), n);
+    stage_store<K8, V8>(st, tid, stage_at(1));
+    stage_load<K8, V8>(rs, lo, (t2_ < nkt ? t2_ : t0_) * KT, st);
     __syncthreads();
     f32x16 S0[2], S1[2];
-    qk(0, S0);
+    qk_plain(0, S0);
     int tj = t0_, tj1 = t1_, tj2 = t2_;
+    uint32_t kqj = kq0, kqj1 = kq1, kqj2 = kq2;
     int j3 = 0;   // ring stage of tile j
 
     auto iteration = [&](f32x16* Sc, f32x16* Sn) {
-      const int tj3 = tj2 < nkt ? next_tile(tj2 + 1) : nkt;
+      uint32_t kqj3 = 7u;
+      const int tj3 = tj2 < nkt ? next_tile(tj2 + 1, kqj3) : nkt;
       __syncthreads();
-      mask_tile(tj, Sc);
-      // --- softmax statistics of tile j ---
-      float mx = Sc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, Sc[kb][v]);
-      mx = fmaxf(mx, lane_read_f(mx, lane ^ 32)) * c_log2;
-      // The running maximum only moves when the tile maximum exceeds it by
-      // more than 8 (log2 units): weights stay below 2^8, exact enough in
-      // fp16, and the accumulator is rescaled only on those tiles.
-      const bool move = mx > m_run + 8.f;
-      const float mn = move ? mx : m_run;
-      const float alpha = move ? fast_exp2(m_run - mn) : 1.f;
-      m_run = mn;
-      // Rescale before the interleaved blocks, so that no branch separates the
-      // weights of tile j from the PV block that consumes them.
-      if (__any(move)) {
-        asm volatile("" ::: "memory");   // keep this a real (rare) branch
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db] = o[db] * alpha;
-      }
+      mask_tile(tj, kqj, Sc);
 
       // The staged tile j+2 (past the last tile the staged registers repeat a
-      // valid tile): zero its V scales past the sequence end.  Both rare
-      // branches sit here so no branch splits the interleaved blocks below.
+      // valid tile): zero its V scales past the sequence end (rare).
       const int skt0 = (tj2 < nkt ? tj2 : t0_) * KT;
       if (skt0 + KT > n) {
         asm volatile("" ::: "memory");
@@ -394,109 +458,137 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
       }
 
       // --- QK^T(j+1) interleaved with the weights of tile j ---
-      // MFMA i uses accumulator kb = i % 2 and k-step ks = i / 2; its LDS
-      // operand is read PF_RA MFMAs ahead; the weights of elements 2i, 2i+1 of
-      // S(j) are computed behind it.  Past the last tile the MFMAs recompute
-      // a resident stage (result unused).
-      const uint8_t* kl = reinterpret_cast<const uint8_t*>(stage_at(ring_next(j3)));
-      auto kread = [&](int i) -> u32x4 {
-        const int kb = i & 1, ks = i >> 1;
-        return *reinterpret_cast<const u32x4*>(kl + (32 * kb + i32) * KS_STRIDE + (16 * ks + 8 * hb) * 2);
-      };
+      // MFMA i (i < 16): accumulator kb = i % 2, k-step ks = i / 2; its LDS
+      // operand is read three MFMAs ahead.  The weights of pair q (elements
+      // 2q, 2q+1 of S(j)) go through three slices so that no instruction
+      // waits on the one before it: the exponent argument in slice q, the
+      // exponential in slice q + 1, the fp16 rounding and the row sum in slice
+      // q + 2.  Past the last tile the MFMAs recompute a resident stage
+      // (result unused).
+      half8 pk[4];  // PV k-steps
+      float ls = 0.f;
+      {
+        const uint8_t* kl = reinterpret_cast<const uint8_t*>(stage_at(ring_next(j3)));
+        auto kread = [&](int i) -> u32x4 {
+          const int kb = i & 1, ks = i >> 1;
+          return *reinterpret_cast<const u32x4*>(kl + (32 * kb + i32) * KS_STRIDE +
+                                                 (16 * ks + 8 * hb) * 2);
+        };
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) Sn[kb][v] = 0.f;
-      half8 pk[4];  // PV k-steps (kb, half)
-      float lsum = 0.f;
-      const half2v ones = half2v{(_Float16)1.f, (_Float16)1.f};
-      // Slice i: weights of elements 2i, 2i+1 in fp32; the fp16 rounding and
-      // the row sum of pair i-1 (one slice later, behind the MFMA, so no
-      // dependent instruction follows its producer directly).
-      float e0 = 0.f, e1 = 0.f;
-      u32x4 kv[16];
+          for (int v = 0; v < 16; ++v) Sn[kb][v] = 0.f;
+        const half2v ones = half2v{(_Float16)1.f, (_Float16)1.f};
+        const float mn = m_run;
+        u32x4 kv[16];
+        float xa[16][2], ea[16][2];
 #pragma unroll
-      for (int i = 0; i < PF_RA; ++i) kv[i] = kread(i);
+        for (int i = 0; i < 3; ++i) kv[i] = kread(i);
 #pragma unroll
-      for (int i = 0; i <= 16; ++i) {
-        if (i < 16) {
-          if (i + PF_RA < 16) kv[i + PF_RA] = kread(i + PF_RA);
-          Sn[i & 1] = mfma32x32x16(u4_to_h8(kv[i]), qreg[i >> 1], Sn[i & 1]);
+        for (int i = 0; i < 18; ++i) {
+          if (i < 16) {
+            if (i + 3 < 16) kv[i + 3] = kread(i + 3);
+            Sn[i & 1] = mfma32x32x16(u4_to_h8(kv[i]), qreg[i >> 1], Sn[i & 1]);
+          }
+          if (i >= 2) {
+            const int q = i - 2, kb = q >> 3, v = 2 * (q & 7);
+            const half2v hp = half2v{(_Float16)ea[q][0], (_Float16)ea[q][1]};
+            pk[2 * kb + (v >> 3)][v & 7] = hp[0];
+            pk[2 * kb + (v >> 3)][(v & 7) + 1] = hp[1];
+            ls = __builtin_amdgcn_fdot2(hp, ones, ls, false);
+          }
+          if (i >= 1 && i <= 16) {
+            const int q = i - 1;
+            ea[q][0] = fast_exp2(xa[q][0]);
+            ea[q][1] = fast_exp2(xa[q][1]);
+          }
+          if (i < 16) {
+            const int kb = i >> 3, v = 2 * (i & 7);
+            xa[i][0] = fmaf(Sc[kb][v], c_log2, -mn);
+            xa[i][1] = fmaf(Sc[kb][v + 1], c_log2, -mn);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        half2v hp;
-        if (i > 0) {
-          const int ip = i - 1, kbp = ip >> 3, vp = 2 * (ip & 7);
-          hp = half2v{(_Float16)e0, (_Float16)e1};
-          pk[2 * kbp + (vp >> 3)][vp & 7] = hp[0];
-          pk[2 * kbp + (vp >> 3)][(vp & 7) + 1] = hp[1];
-        }
-        if (i < 16) {
-          const int kb = i >> 3, v = 2 * (i & 7);
-          e0 = fast_exp2(fmaf(Sc[kb][v], c_log2, -mn));
-          e1 = fast_exp2(fmaf(Sc[kb][v + 1], c_log2, -mn));
-        }
-        if (i > 0) lsum = __builtin_amdgcn_fdot2(hp, ones, lsum, false);
-        __builtin_amdgcn_sched_barrier(0);
       }
-      l_run = fmaf(l_run, alpha, lsum);
+      // every weight is computed here (nothing of the block sinks into the
+      // rare branch below)
+      asm volatile("" : "+v"(ls), "+v"(pk[0]), "+v"(pk[1]), "+v"(pk[2]), "+v"(pk[3]));
+      // Rare: a lane's weight sum beyond the fp16-safe limit (also every
+      // row's first tile, whose m starts at -1e30): take the row maximum,
+      // move m, rescale and recompute the weights.
+      if (__builtin_amdgcn_ballot_w64(!(ls <= P_SUM_LIMIT)) != 0) {
+        asm volatile("" : "+v"(Sc[0]), "+v"(Sc[1]));   // keep this path in its branch
+        ls = rescale(Sc, pk);
+      }
+      l_run += ls;
 
       // --- PV(j) interleaved with the dequantisation of tile j+2 ---
-      // MFMA i uses accumulator db = i % 4 and k-step kk = i / 4; pair i of the
-      // staged tile (K pairs 0..7, then V pairs 0..7) is dequantised behind it.
+      // MFMA i (i < 16): accumulator db = i % 4, k-step kk = i / 4.  Pair q
+      // of the staged tile (K pairs 0..7, then V pairs 0..7) goes through
+      // three slices: codes to biased fp16 in slice q, minus the biased
+      // zero-point in slice q + 1, times the scale in slice q + 2.
       {
         const uint8_t* vl = reinterpret_cast<const uint8_t*>(stage_at(j3)) + LDS_K;
         auto vread = [&](int i) -> u32x4 {
           const int db = i & 3, kk = i >> 2;
-          return *reinterpret_cast<const u32x4*>(vl + (32 * db + i32) * VS_STRIDE + (16 * kk + 8 * hb) * 2);
+          return *reinterpret_cast<const u32x4*>(vl + (32 * db + i32) * VS_STRIDE +
+                                                 (16 * kk + 8 * hb) * 2);
         };
         char* sdst = stage_at(ring_prev(j3));
         const int unit = tid >> 1, khalf = tid & 1;
         const int kkey = unit >> 2, kgrp = unit & 3;
         const int vd = tid >> 2, vq = tid & 3;
-        const half2v knz = u32_to_h2(neg_biased_zero_h2(st.kz));
+        const uint32_t knz = neg_biased_zero_h2(st.kz);
         const _Float16 ksc = bits_to_half((uint16_t)st.ks);
-        const half2v ks2 = half2v{ksc, ksc};
-        const uint32_t ks2u = h2_to_u32(ks2);
-        u32x4 ko0, ko1, vo0, vo1;
+        const uint32_t ks2 = h2_to_u32(half2v{ksc, ksc});
+        u32x4 ko[2], vo[2];
         u32x4 av[16];
+        uint32_t cb[16], cz[16], nzv[8];
 #pragma unroll
-        for (int i = 0; i < PF_RA; ++i) av[i] = vread(i);
-        // Slice i: MFMA i, the scaling of pair i-1 and the centring of pair i.
-        uint32_t cen = 0;
+        for (int i = 0; i < 3; ++i) av[i] = vread(i);
 #pragma unroll
-        for (int i = 0; i <= 16; ++i) {
+        for (int i = 0; i < 18; ++i) {
           if (i < 16) {
-            if (i + PF_RA < 16) av[i + PF_RA] = vread(i + PF_RA);
+            if (i + 3 < 16) av[i + 3] = vread(i + 3);
             o[i & 3] = mfma32x32x16(u4_to_h8(av[i]), pk[i >> 2], o[i & 3]);
           }
-          if (i > 0) {
-            const int ip = i - 1;
-            if (ip < 8) {
-              const uint32_t w = h2_mul(cen, ks2u);
-              if (ip < 4) ko0[ip] = w; else ko1[ip - 4] = w;
+          if (i >= 2) {
+            const int q = i - 2;
+            if (q < 8) {
+              ko[q >> 2][q & 3] = h2_mul(cz[q], ks2);
             } else {
-              const int jv = ip - 8;
-              const uint32_t w = h2_mul(cen, v_scales(st, jv));
-              if (vslot(jv) < 4) vo0[vslot(jv)] = w; else vo1[vslot(jv) - 4] = w;
+              const int jv = q - 8;
+              vo[vslot(jv) >> 2][vslot(jv) & 3] = h2_mul(cz[q], v_scales(st, jv));
             }
           }
-          if (i < 8) cen = k_centered<K8>(st, i, knz);
-          else if (i < 16) cen = v_centered<V8>(st, i - 8);
-          if (i == 8) {
-            u32x4* kd = reinterpret_cast<u32x4*>(sdst + kkey * KS_STRIDE + (32 * kgrp + 16 * khalf) * 2);
-            kd[0] = ko0;
-            kd[1] = ko1;
+          if (i >= 1 && i <= 16) {
+            const int q = i - 1;
+            cz[q] = h2_add(cb[q], q < 8 ? knz : nzv[q - 8]);
           }
-          if (i == 16) {
+          if (i < 16) {
+            if (i < 8) {
+              cb[i] = k_biased<K8>(st, i);
+            } else {
+              cb[i] = v_biased<V8>(st, i - 8);
+              nzv[i - 8] = v_negzero(st, i - 8);
+            }
+          }
+          if (i == 10) {
+            u32x4* kd = reinterpret_cast<u32x4*>(sdst + kkey * KS_STRIDE + (32 * kgrp + 16 * khalf) * 2);
+            kd[0] = ko[0];
+            kd[1] = ko[1];
+          }
+          if (i == 17) {
             u32x4* vdst = reinterpret_cast<u32x4*>(sdst + LDS_K + vd * VS_STRIDE + 32 * vq);
-            vdst[0] = vo0;
-            vdst[1] = vo1;
+            vdst[0] = vo[0];
+            vdst[1] = vo[1];
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      stage_load<K8, V8>(c, (tj3 < nkt ? tj3 : t0_) * KT, st);
+      stage_load<K8, V8>(rs, lo, (tj3 < nkt ? tj3 : t0_) * KT, st);
       tj = tj1; tj1 = tj2; tj2 = tj3;
+      kqj = kqj1; kqj1 = kqj2; kqj2 = kqj3;
       j3 = ring_next(j3);
     };
 
@@ -550,9 +642,9 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
 // XCDs, so with the KV head as the fastest index every XCD keeps serving the
 // same KV heads (its L2 holds their K/V tiles); query blocks run longest-first.
 template <int R, bool K8, bool V8>
-__global__ void __launch_bounds__(NT)
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[3 * LDS_STAGE];
+  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * LDS_STAGE];
   const int H = a.nheads, B = a.k.B;
   const int id = blockIdx.x;
   const int g = a.heads[id % H];
@@ -620,15 +712,12 @@ int prefill_splits(int B, int Hkv, int r, int q_len, int max_len) {
   // Enough workgroups to cover the CUs once, each split keeping >= 4 key tiles:
   // the kernel's LDS admits one workgroup per CU, so one round of longer
   // splits beats two rounds of shorter ones (half the partials to write and
-  // merge; 512-row chunk after 8192 cached: 118 -> 104 us).
-  const int bq = 32 * (NWAVE / r);
+  // merge).
+  const int bq = 32 * (NBLK / r);
   const int64_t wgs = (int64_t)B * Hkv * ((q_len + bq - 1) / bq);
   const int tiles = (max_len + KT - 1) / KT;
-#ifndef TAQ_PREFILL_SPLIT_TARGET
-#define TAQ_PREFILL_SPLIT_TARGET 256
-#endif
   int ns = 1;
-  while (ns < 16 && wgs * ns < TAQ_PREFILL_SPLIT_TARGET && tiles / (2 * ns) >= 4) ns *= 2;
+  while (ns < 16 && wgs * ns < 256 && tiles / (2 * ns) >= 4) ns *= 2;
   return ns;
 }
 
