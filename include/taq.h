@@ -14,7 +14,8 @@
  * section 3.2: group size 32) and dequantised inside the tile load (section
  * 1.3: dequantise on read instead of a separate pass), with KV-tile skipping
  * driven by a block mask (section 2.3).  Query head h reads KV head
- * h / (num_q_heads / num_kv_heads) (grouped-query attention).
+ * h / (num_q_heads / num_kv_heads) (grouped-query attention).  Below, "the
+ * m.xxqk.cn page" and "the xdnf.cn page" name these two sources.
  *
  * Quantisation of one group x[0..31] (32 consecutive head_dim channels of one
  * token of one KV head), qmax = 2^bits - 1:
@@ -132,7 +133,7 @@ size_t taq_kv_codes_bytes(const taq_kv_cache* cache);
 size_t taq_kv_meta_count(const taq_kv_cache* cache);
 
 /* Quantise fp16 x [B][Hkv][count][D] into tokens start .. start+count-1 of
- * every (batch, head) of `cache` (section 2.4 of the KV-quantisation page).
+ * every (batch, head) of `cache` (section 2.4 of the xdnf.cn page).
  * Codes, scales and zeros of other tokens are left unchanged.  Bit-exact with
  * the definition at the top of this file.  Errors: INVALID_ARGUMENT (null
  * pointer, start/count out of [0, capacity], bad shape), UNSUPPORTED (bits not
@@ -157,7 +158,7 @@ taq_status taq_kv_quantize_pair(const taq_kv_cache* k_cache, const taq_kv_cache*
  * x[b][h][0 .. count-1] going to cache positions starts[b] .. starts[b] +
  * count - 1, so sequences of different lengths each append their next chunk
  * in one call (the quantisation happens as tokens enter the cache, section
- * 1.3 of the KV-quantisation page).  starts is a device int32 [B]; positions
+ * 1.3 of the xdnf.cn page).  starts is a device int32 [B]; positions
  * outside [0, capacity) are skipped on the device (the host cannot check
  * device values), and an odd int4 start rewrites only the new token's nibble
  * of the shared V byte.  Errors: INVALID_ARGUMENT (null pointer, count
@@ -167,7 +168,10 @@ taq_status taq_kv_append(const taq_kv_cache* cache, const void* x_f16,
 
 /* Dequantise tokens start .. start+count-1 into out [B][Hkv][count][D] as
  * fp32 (exact) and/or fp16 (round-to-nearest-even of the exact value); either
- * output may be NULL but not both.  A checking aid for the stored format. */
+ * output may be NULL but not both.  The value of a code is (c - z) * s, the
+ * inverse map of the grouped asymmetric quantisation (section 2.4 of the
+ * xdnf.cn page).  A checking aid for the stored format: the attention calls
+ * apply the same map inside their tile loads. */
 taq_status taq_kv_dequantize(const taq_kv_cache* cache, int32_t start,
                              int32_t count, float* out_f32, void* out_f16,
                              void* stream);
@@ -180,7 +184,12 @@ size_t taq_attn_decode_workspace_bytes(const taq_kv_cache* k_cache,
 /* Single-token decode: for each batch entry b and query head h, attention of
  * q[b][h] over keys 0 .. seq_lens[b]-1 of KV head h / (Hq/Hkv) (the new
  * token is already in the cache), skipping KV tiles the mask drops
- * (n_q_tiles == 1).  Split over KV chunks; the partial (max, normaliser,
+ * (n_q_tiles must be 1, else INVALID_ARGUMENT).  What is computed:
+ * softmax(q K^T * scale) V, the scaled dot-product attention of section 3.1
+ * of the m.xxqk.cn page, with K and V the dequantised cache values (section
+ * 2.4 of the xdnf.cn page), reduced tile by tile with the running
+ * (maximum, normaliser) merge of section 2.2 of the xdnf.cn page and with the
+ * tiles that the block mask of its section 2.3 drops left out.  Split over KV chunks; the partial (max, normaliser,
  * accumulator) triples are merged in a fixed order, so results are bitwise
  * repeatable.  k_cache must use TAQ_LAYOUT_TOKEN and v_cache
  * TAQ_LAYOUT_CHANNEL, with equal geometry; head_dim must be 128; num_q_heads /
@@ -199,7 +208,7 @@ taq_status taq_attn_decode(const taq_kv_cache* k_cache,
  * exp(s - max) v and exp(s - max) against that fixed maximum with no
  * rescaling, and the chunk partials are added.  This is the plain reading of
  * the "coarse maximum first, then correct the normaliser" wording of section
- * 2.2 of the block-sparse page, kept as an ablation and cross-check of the
+ * 2.2 of the xdnf.cn page, kept as an ablation and cross-check of the
  * online merge that taq_attn_decode uses (it reads K twice).  Arguments,
  * workspace size and errors as taq_attn_decode. */
 taq_status taq_attn_decode_two_pass(const taq_kv_cache* k_cache,
@@ -236,8 +245,14 @@ taq_status taq_attn_decode_noalloc(const taq_kv_cache* k_cache,
 
 /* Causal prefill with equal query and key lengths: q/o [B][Hq][L][D] where
  * L = max_seq_len; row i of batch b attends to keys j <= i, j < seq_lens[b],
- * in tiles the mask keeps (NULL = dense causal).  Query-row tiles whose whole
- * KV range is skipped cost nothing.  Same cache requirements as decode. */
+ * in tiles the mask keeps (NULL = dense causal).  Row by row this is the
+ * causal scaled dot-product attention of section 3.1 of the m.xxqk.cn page
+ * over the dequantised cache (section 2.4 of the xdnf.cn page), computed per
+ * 128x128 tile with the online softmax merge of section 2.2 of the xdnf.cn
+ * page; tiles dropped by the block mask (its section 2.3) contribute nothing,
+ * and query-row tiles whose whole KV range is skipped cost nothing.  Same
+ * cache requirements as decode; mask n_q_tiles and n_k_tiles must both cover
+ * ceil(max_seq_len / 128). */
 taq_status taq_attn_prefill(const taq_kv_cache* k_cache,
                             const taq_kv_cache* v_cache, const void* q_f16,
                             int32_t num_q_heads, const int32_t* seq_lens,
@@ -256,7 +271,7 @@ size_t taq_attn_prefill_chunk_workspace_bytes(const taq_kv_cache* k_cache,
  * sits at position p = seq_lens[b] - q_len + i (bottom-right alignment) and
  * attends to keys j <= p in tiles the mask keeps, the mask being indexed by
  * positions; rows with p < 0 are written as zeros.  This is the step of the
- * multi-turn setting that section 4.2 of the KV-quantisation page discusses:
+ * multi-turn setting that section 4.2 of the xdnf.cn page discusses:
  * a new turn reads the quantised history through the same tiled kernel.
  * q_len must lie in [0, max_seq_len]; everything else as taq_attn_prefill,
  * which is the case q_len = max_seq_len with every seq_lens[b] =
@@ -280,7 +295,7 @@ size_t taq_tile_mask_workspace_bytes(const taq_kv_cache* k_cache,
                                      int32_t max_seq_len);
 
 /* Training-free KV-tile mask for block-sparse prefill, after the policy of
- * section 2.3 of the block-sparse page: a coarse pattern of skipped 128x128
+ * section 2.3 of the xdnf.cn page: a coarse pattern of skipped 128x128
  * blocks with dense local blocks and a capped skipped share.  That page
  * predicts the pattern with a learned head; this call scores tiles from the
  * data instead.  For batch entry b (n = seq_lens[b], nt_b = ceil(n / 128)),
@@ -316,7 +331,7 @@ size_t taq_head_sensitivity_workspace_bytes(int32_t batch, int32_t num_kv_heads,
                                             int32_t num_q_heads, int32_t max_seq_len);
 
 /* Per-KV-head precision assignment from measured sensitivity (section 2.4 of
- * the block-sparse page: sensitive heads are stored at higher precision, the
+ * the xdnf.cn page: sensitive heads are stored at higher precision, the
  * others with fewer bits; section 3.4: more high-precision heads, less memory
  * saved).  The page leaves the score open; here the score of KV head g is how
  * far its decode outputs move when its cache drops from int8 to int4:

@@ -169,6 +169,22 @@ def test_attention_rejects(call):
     assert call(mask=nodata)[0] == INVALID
 
 
+@pytest.mark.parametrize("call", [decode_call, decode_two_pass_call, decode_noalloc_call])
+def test_decode_mask_must_have_one_query_tile(call):
+    """A decode mask is one row of KV tiles: any other n_q_tiles is an argument
+    error, not a mask read with the wrong row stride."""
+    for nq in (2, 3):
+        rc, msg = call(mask=T._Mask(FAKE, 128, nq, 2, 0, 0))
+        assert rc == INVALID and "n_q_tiles" in msg, (nq, msg)
+    assert call(mask=T._Mask(FAKE, 128, 0, 2, 0, 0))[0] == INVALID
+    if not os.path.exists("/dev/kfd"):
+        rc, msg = call(mask=T._Mask(FAKE, 128, 1, 2, 0, 0))
+        assert rc == HIP, msg
+        # the same two-row mask is a valid prefill mask
+        rc, msg = prefill_call(mask=T._Mask(FAKE, 128, 2, 2, 0, 0))
+        assert rc == HIP, msg
+
+
 def test_decode_workspace_too_small():
     assert decode_call(ws_bytes=16)[0] == WS_SMALL
     assert decode_call(ws=0)[0] == WS_SMALL

@@ -283,7 +283,12 @@ taq_status decode_validate(const taq_kv_cache* k, const taq_kv_cache* v, const v
     return fail(TAQ_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
   if (softmax_scale < 0.f)
     return fail(TAQ_ERR_UNSUPPORTED, "softmax_scale must be >= 0 (0 selects 1/sqrt(head_dim))");
-  return check_mask(mask, 1, (max_len + TAQ_TILE - 1) / TAQ_TILE);
+  st = check_mask(mask, 1, (max_len + TAQ_TILE - 1) / TAQ_TILE);
+  if (st) return st;
+  if (mask && mask->n_q_tiles != 1)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "mask: decode takes n_q_tiles == 1, got %d",
+                mask->n_q_tiles);
+  return TAQ_OK;
 }
 
 // Shared body of taq_attn_decode (online softmax), taq_attn_decode_two_pass

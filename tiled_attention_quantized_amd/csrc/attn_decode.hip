@@ -675,16 +675,11 @@ decode_split_kernel(DecodeArgs a) {
   __shared__ float lds[2 * WAVES * R + WAVES * R * D];
   __shared__ __attribute__((aligned(16))) uint32_t vstage[WAVES * (V8 ? 1024 : 512)];
   const int units = a.k.B * a.nheads;
-#ifdef TAQ_DECODE_CHUNK_FASTEST
-  const int u = blockIdx.x / a.nchunk;
-  const int c = blockIdx.x - u * a.nchunk;
-#else
   // highest chunk index first: the later chunks exist only for the longest
   // sequences, so they start early and the short final chunks fill the end
   // (ragged lengths: 238 -> 235 us)
   const int c = a.nchunk - 1 - (int)(blockIdx.x / units);
   const int u = blockIdx.x - (a.nchunk - 1 - c) * units;
-#endif
   const int b = u / a.nheads;
   const int g = a.heads[u - b * a.nheads];
   int n = a.lens[b];
