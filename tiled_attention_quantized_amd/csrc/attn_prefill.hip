@@ -14,27 +14,31 @@
 //    query rows of all r = Hq/Hkv query heads that share one KV head, so every
 //    K/V tile is fetched and dequantised once for 256 (head, row) pairs; wave w
 //    takes head w % r and the 32 rows (w / r) * 32 .. +31;
-//  * the key loop runs over the workgroup's needed 64-key tiles through three
-//    LDS stages as a software pipeline with one barrier per tile: the QK^T
-//    MFMAs of tile j+1 interleave with the weights of tile j, and the PV MFMAs
-//    of tile j with the dequantisation of tile j+2; tile j+3 is fetched into
-//    registers.  Inside those blocks each chain of dependent vector
-//    instructions (exponent argument, exponential, fp16 rounding and row sum;
-//    codes to fp16, zero-point, scale) is spread over three matrix-instruction
-//    slices, so no instruction waits on the one just before it;
+//  * the key loop runs over the workgroup's needed 64-key tiles through LDS
+//    rings of four stages as a software pipeline with one barrier per tile:
+//    the QK^T MFMAs of tile j+1 interleave with the weights of tile j, and
+//    the PV MFMAs of tile j with the dequantisation of tile j+3; tile j+4 is
+//    fetched into registers.  The two waves of a SIMD take the barrier at
+//    different points of that sequence, so while one computes exponentials
+//    the other dequantises.  Inside those blocks each chain of dependent
+//    vector instructions (exponent argument, exponential, fp16 rounding and
+//    row sum; codes to fp16, zero-point, scale) is spread over three
+//    matrix-instruction slices, so no instruction waits on the one just
+//    before it;
 //  * both contractions use v_mfma_f32_32x32x16_f16 in transposed form:
 //    S^T = K-hat Q^T (A = K-hat tile from LDS, B = Q held in registers) and
 //    O^T += V-hat^T P^T (A = V-hat^T tile from LDS, B = P straight from the
 //    S^T accumulator), so every lane owns one query row for the whole loop and
 //    the softmax statistics stay lane-local;
-//  * the running maximum m of a row is not recomputed per tile: the weights
-//    exp2(s - m) of a tile are formed against the current m and rounded to
-//    fp16, and only when a lane's sum of them exceeds 2^15 (a score more than
-//    ~15 above m, or the row's first tile, whose m starts at -1e30) is the
-//    tile's row maximum taken, m moved, the accumulator and normaliser
-//    rescaled and the weights recomputed (a rare branch).  The result is the
-//    same softmax: the factor exp2(-m) cancels between numerator and
-//    normaliser;
+//  * the running maximum m of a row is not recomputed per tile: it starts
+//    at the row maximum of the first tile, the weights exp2(s - m) of each
+//    tile are formed against the current m and rounded to fp16, and only when
+//    a lane's sum of them exceeds 2^15 (a score more than ~15 above m, or a
+//    row's first key after tiles that gave it none) is the tile's row maximum
+//    taken, m moved, the accumulator and normaliser rescaled and the weights
+//    recomputed (a rare branch that forms the tile's scores again).  The
+//    result is the same softmax: the factor exp2(-m) cancels between
+//    numerator and normaliser;
 //  * the needed tiles are found from scalar bit windows over 32 mask tiles
 //    (one vector load and ballot per window and query tile), and the
 //    causal / length / mask masking of a tile's scores only runs on tiles
@@ -55,8 +59,12 @@ constexpr int KS_STRIDE = D * 2 + 16;  // bytes per K-hat row in LDS (padded)
 constexpr int VS_STRIDE = KT * 2 + 16; // bytes per V-hat^T row in LDS (padded)
 constexpr int LDS_K = KT * KS_STRIDE;
 constexpr int LDS_V = D * VS_STRIDE;
-constexpr int LDS_STAGE = LDS_K + LDS_V;   // one tile (K-hat and V-hat^T)
-constexpr int NSTAGE = 3;
+// LDS rings of four stages each for K-hat and V-hat^T tiles (walk tile j in
+// stage j % 4), then one int per wave for the SIMD table.
+constexpr int NKST = 4;
+constexpr int NVST = 4;
+constexpr int LDS_TABLE = NKST * LDS_K + NVST * LDS_V;
+constexpr int LDS_BYTES = LDS_TABLE + 4 * NWAVE;
 constexpr float NEG_BIG = -1.0e30f;
 // A lane's weights of one tile are safe in fp16 (and exact enough) while
 // their sum stays at or below this; above it the tile takes the rescale path.
@@ -130,7 +138,12 @@ __device__ __forceinline__ LaneOff lane_offsets(int tid, int cap) {
 }
 
 template <bool K8, bool V8>
-__device__ __forceinline__ void stage_load(const Bases& r, const LaneOff& o, int kt0, Staged& s) {
+__device__ __forceinline__ void stage_load(const Bases& r, const LaneOff& o_in, int kt0, Staged& s) {
+  // The lane offsets are opaque here, so the compiler keeps each address as
+  // scalar base plus 32-bit lane offset instead of hoisting 64-bit per-lane
+  // pointers (two registers each) out of the tile loop.
+  LaneOff o = o_in;
+  asm volatile("" : "+v"(o.k), "+v"(o.km), "+v"(o.v), "+v"(o.vm));
   const uint32_t tk = (uint32_t)kt0 * (K8 ? D : D / 2);
   if (K8) {
     s.kc = load_at<u32x4>(r.k, tk, o.k);
@@ -191,7 +204,7 @@ __device__ __forceinline__ void zero_tail_scales(Staged& s, int key0, int n) {
 
 // Dequantise the staged registers into LDS stage `dst` in one go (prologue).
 template <bool K8, bool V8>
-__device__ __forceinline__ void stage_store(const Staged& s, int tid, char* dst) {
+__device__ __forceinline__ void stage_store(const Staged& s, int tid, char* kdst, char* vdst) {
   const uint32_t knz = neg_biased_zero_h2(s.kz);
   const _Float16 ksc = bits_to_half((uint16_t)s.ks);
   const uint32_t ks2 = h2_to_u32(half2v{ksc, ksc});
@@ -200,7 +213,7 @@ __device__ __forceinline__ void stage_store(const Staged& s, int tid, char* dst)
   u32x4 ko[2];
 #pragma unroll
   for (int j = 0; j < 8; ++j) ko[j >> 2][j & 3] = h2_mul(h2_add(k_biased<K8>(s, j), knz), ks2);
-  u32x4* kd = reinterpret_cast<u32x4*>(dst + key * KS_STRIDE + (32 * grp + 16 * half) * 2);
+  u32x4* kd = reinterpret_cast<u32x4*>(kdst + key * KS_STRIDE + (32 * grp + 16 * half) * 2);
   kd[0] = ko[0];
   kd[1] = ko[1];
   const int d = tid >> 2, q = tid & 3;
@@ -209,7 +222,7 @@ __device__ __forceinline__ void stage_store(const Staged& s, int tid, char* dst)
   for (int j = 0; j < 8; ++j)
     vo[vslot(j) >> 2][vslot(j) & 3] = h2_mul(h2_add(v_biased<V8>(s, j), v_negzero(s, j)),
                                              v_scales(s, j));
-  u32x4* vd = reinterpret_cast<u32x4*>(dst + LDS_K + d * VS_STRIDE + 32 * q);
+  u32x4* vd = reinterpret_cast<u32x4*>(vdst + d * VS_STRIDE + 32 * q);
   vd[0] = vo[0];
   vd[1] = vo[1];
 }
@@ -345,13 +358,12 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
 
   const float c_log2 = a.scale_log2;   // > 0 (checked on the host)
 
-  auto stage_at = [&](int x) -> char* { return lds + x * LDS_STAGE; };
-  auto ring_next = [](int x) { return x == 2 ? 0 : x + 1; };
-  auto ring_prev = [](int x) { return x == 0 ? 2 : x - 1; };
+  auto kstage = [&](int x) -> char* { return lds + x * LDS_K; };
+  auto vstage = [&](int x) -> char* { return lds + NKST * LDS_K + x * LDS_V; };
 
-  // S^T = K-hat Q^T for the tile in stage x (16 MFMAs), no interleaving
-  auto qk_plain = [&](int x, f32x16* S) {
-    const uint8_t* kl = reinterpret_cast<const uint8_t*>(stage_at(x));
+  // S^T = K-hat Q^T for the tile whose K-hat is at kl (16 MFMAs), no interleaving
+  auto qk_plain = [&](const char* kl8, f32x16* S) {
+    const uint8_t* kl = reinterpret_cast<const uint8_t*>(kl8);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -384,9 +396,10 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
   };
 
   // Rare path: the tile's row maximum (both lane halves of the row), m moved
-  // to it if larger, accumulator and normaliser rescaled, weights recomputed
-  // into pk; returns the lane's row sum of the new fp16 weights.
-  auto rescale = [&](const f32x16* S, half8 (&pk)[4]) -> float {
+  // to it if larger, the normaliser rescaled, weights recomputed into pk;
+  // returns the lane's row sum of the new fp16 weights and, in alpha, the
+  // factor that the accumulator still has to be multiplied by.
+  auto rescale = [&](const f32x16* S, half8 (&pk)[4], float& alpha) -> float {
     float mx = S[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -394,11 +407,9 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kb][v]);
     mx = fmaxf(mx, lane_read_f(mx, lane ^ 32)) * c_log2;
     const float mn = fmaxf(m_run, mx);     // rows with no key keep NEG_BIG
-    const float alpha = fast_exp2(m_run - mn);
+    alpha = fast_exp2(m_run - mn);
     m_run = mn;
     l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db] = o[db] * alpha;
     const half2v ones = half2v{(_Float16)1.f, (_Float16)1.f};
     float ls = 0.f;
 #pragma unroll
@@ -416,180 +427,234 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
   };
 
   // ---- software pipeline over the workgroup's KV tiles -------------------------
-  // Tiles t_0, t_1, ... (causal and mask order) go through three LDS stages.
-  // Iteration j (one barrier): the QK^T MFMAs of tile j+1 run interleaved with
-  // the weights of tile j, then the PV MFMAs of tile j run interleaved with the
-  // dequantisation of tile j+2 into the third stage; tile j+3 is fetched from
-  // HBM into registers.  Every wave walks the same tiles; rows a tile does not
-  // reach are masked, so the loop has no per-wave branches.
-  uint32_t kq0, kq1 = 7u, kq2 = 7u;
+  // Tiles t_0, t_1, ... (causal and mask order) go through the LDS rings.
+  // Per tile j every wave runs two interleaved blocks, in this order:
+  //   QK(j): the QK^T MFMAs of tile j+1 with the weights of tile j;
+  //   PV(j): the PV MFMAs of tile j with the dequantisation of a staged tile.
+  // One barrier per tile separates epochs.  The first wave of each SIMD
+  // ("early") takes the barrier before QK(j), the second ("late") between
+  // QK(j) and PV(j), so epoch e holds the early waves' QK(e-1) and PV(e-1)
+  // and the late waves' PV(e-1) and QK(e).  In each half of an epoch one wave
+  // of a SIMD computes exponentials (vector-heavy) while the other
+  // dequantises (vector-light), and both keep the matrix unit busy.  In
+  // epoch e the waves read K-hat of tiles e and e+1 (e-1 and e on the rare
+  // path) and V-hat^T of tile e-1, and write tile e+2 (dequantised in PV(e-1)
+  // from the tile staged three ahead), so four stages of each ring are in
+  // use.  Tiles are fetched from HBM into registers one tile ahead of their
+  // dequantisation.  Every wave walks the same tiles; rows a tile does not
+  // reach are masked, so the loop has no per-wave branches other than the
+  // barrier's place.
+  uint32_t kq0, kq1 = 7u, kq2 = 7u, kq3 = 7u, kq4 = 7u;
   const int t0_ = next_tile(kt_lo, kq0);
   if (t0_ < nkt) {
+    // tile window: walk tiles j .. j+4 (nkt past the end) and their keep bits
     const int t1_ = next_tile(t0_ + 1, kq1);
     const int t2_ = t1_ < nkt ? next_tile(t1_ + 1, kq2) : nkt;
+    const int t3_ = t2_ < nkt ? next_tile(t2_ + 1, kq3) : nkt;
+    const int t4_ = t3_ < nkt ? next_tile(t3_ + 1, kq4) : nkt;
+    // SIMD of each wave (hardware wave id register, SIMD field); a wave is
+    // late when an earlier wave of the workgroup sits on the same SIMD
+    int* simd_of = reinterpret_cast<int*>(lds + LDS_TABLE);
+    if (lane == 0) simd_of[w] = (int)__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4);
+    // a tile past the end is staged as a copy of a valid one (never read)
+    auto valid = [&](int t) { return t < nkt ? t : t0_; };
+    auto stage_direct = [&](int t, int kx, int vx, Staged& s) {
+      stage_load<K8, V8>(rs, lo, valid(t) * KT, s);
+      if (valid(t) * KT + KT > n) zero_tail_scales(s, valid(t) * KT + 16 * (tid & 3), n);
+      stage_store<K8, V8>(s, tid, kstage(kx), vstage(vx));
+    };
     Staged st;
-    stage_load<K8, V8>(rs, lo, t0_ * KT, st);
-    if (t0_ * KT + KT > n) zero_tail_scales(st, t0_ * KT + 16 * (tid & 3), n);
-    stage_store<K8, V8>(st, tid, stage_at(0));
-    const int ta = t1_ < nkt ? t1_ : t0_;
-    stage_load<K8, V8>(rs, lo, ta * KT, st);
-    if (ta * KT + KT > n) zero_tail_scales(st, ta * KT + 16 * (tid & 3), n);
-    stage_store<K8, V8>(st, tid, stage_at(1));
-    stage_load<K8, V8>(rs, lo, (t2_ < nkt ? t2_ : t0_) * KT, st);
+    stage_direct(t0_, 0, 0, st);
+    stage_direct(t1_, 1, 1, st);
+    stage_direct(t2_, 2, 2, st);
+    stage_load<K8, V8>(rs, lo, valid(t3_) * KT, st);
     __syncthreads();
+    bool late_b = false;
+    {
+      const int mine = simd_of[w];
+      for (int u = 0; u < w; ++u) late_b |= simd_of[u] == mine;
+    }
+    const bool late = __builtin_amdgcn_readfirstlane((int)late_b) != 0;
+
     f32x16 S0[2], S1[2];
-    qk_plain(0, S0);
-    int tj = t0_, tj1 = t1_, tj2 = t2_;
-    uint32_t kqj = kq0, kqj1 = kq1, kqj2 = kq2;
-    int j3 = 0;   // ring stage of tile j
+    qk_plain(kstage(0), S0);
+    // m starts at the first tile's row maximum, so its weights need no rescale
+    mask_tile(t0_, kq0, S0);
+    {
+      float mx = S0[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S0[kb][v]);
+      mx = fmaxf(mx, lane_read_f(mx, lane ^ 32)) * c_log2;
+      m_run = fmaxf(m_run, mx);   // a row with no key in the tile keeps NEG_BIG
+    }
+    int tj = t0_, tj1 = t1_, tj2 = t2_, tj3 = t3_, tj4 = t4_;
+    uint32_t kqj = kq0, kqj1 = kq1, kqj2 = kq2, kqj3 = kq3, kqj4 = kq4;
+    int jj = 0;   // walk index of tile j
+    half8 pk[4];  // weights of tile j
 
-    auto iteration = [&](f32x16* Sc, f32x16* Sn) {
-      uint32_t kqj3 = 7u;
-      const int tj3 = tj2 < nkt ? next_tile(tj2 + 1, kqj3) : nkt;
-      __syncthreads();
-      mask_tile(tj, kqj, Sc);
-
-      // The staged tile j+2 (past the last tile the staged registers repeat a
-      // valid tile): zero its V scales past the sequence end (rare).
-      const int skt0 = (tj2 < nkt ? tj2 : t0_) * KT;
-      if (skt0 + KT > n) {
-        asm volatile("" ::: "memory");
-        zero_tail_scales(st, skt0 + 16 * (tid & 3), n);
-      }
-
-      // --- QK^T(j+1) interleaved with the weights of tile j ---
-      // MFMA i (i < 16): accumulator kb = i % 2, k-step ks = i / 2; its LDS
-      // operand is read three MFMAs ahead.  The weights of pair q (elements
-      // 2q, 2q+1 of S(j)) go through three slices so that no instruction
-      // waits on the one before it: the exponent argument in slice q, the
-      // exponential in slice q + 1, the fp16 rounding and the row sum in slice
-      // q + 2.  Past the last tile the MFMAs recompute a resident stage
-      // (result unused).
-      half8 pk[4];  // PV k-steps
+    // QK block: S^T of tile j+1 into Sn, the weights of tile j (scores Sc)
+    // into pk; returns the lane's sum of the weights.  MFMA i (i < 16):
+    // accumulator kb = i % 2, k-step ks = i / 2; its LDS operand is read
+    // three MFMAs ahead.  The weights of pair q (elements 2q, 2q+1 of S(j))
+    // go through three slices so that no instruction waits on the one before
+    // it: the exponent argument in slice q, the exponential in slice q + 1,
+    // the fp16 rounding and the row sum in slice q + 2.  Past the last tile
+    // the MFMAs recompute a resident stage (result unused).
+    auto qk_block = [&](const f32x16* Sc, f32x16* Sn) -> float {
       float ls = 0.f;
-      {
-        const uint8_t* kl = reinterpret_cast<const uint8_t*>(stage_at(ring_next(j3)));
-        auto kread = [&](int i) -> u32x4 {
-          const int kb = i & 1, ks = i >> 1;
-          return *reinterpret_cast<const u32x4*>(kl + (32 * kb + i32) * KS_STRIDE +
-                                                 (16 * ks + 8 * hb) * 2);
-        };
+      const uint8_t* kl = reinterpret_cast<const uint8_t*>(kstage((jj + 1) & 3));
+      auto kread = [&](int i) -> u32x4 {
+        const int kb = i & 1, ks = i >> 1;
+        return *reinterpret_cast<const u32x4*>(kl + (32 * kb + i32) * KS_STRIDE +
+                                               (16 * ks + 8 * hb) * 2);
+      };
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) Sn[kb][v] = 0.f;
-        const half2v ones = half2v{(_Float16)1.f, (_Float16)1.f};
-        const float mn = m_run;
-        u32x4 kv[16];
-        float xa[16][2], ea[16][2];
+        for (int v = 0; v < 16; ++v) Sn[kb][v] = 0.f;
+      const half2v ones = half2v{(_Float16)1.f, (_Float16)1.f};
+      const float mn = m_run;
+      u32x4 kv[16];
+      float xa[16][2], ea[16][2];
 #pragma unroll
-        for (int i = 0; i < 3; ++i) kv[i] = kread(i);
+      for (int i = 0; i < 3; ++i) kv[i] = kread(i);
 #pragma unroll
-        for (int i = 0; i < 18; ++i) {
-          if (i < 16) {
-            if (i + 3 < 16) kv[i + 3] = kread(i + 3);
-            Sn[i & 1] = mfma32x32x16(u4_to_h8(kv[i]), qreg[i >> 1], Sn[i & 1]);
-          }
-          if (i >= 2) {
-            const int q = i - 2, kb = q >> 3, v = 2 * (q & 7);
-            const half2v hp = half2v{(_Float16)ea[q][0], (_Float16)ea[q][1]};
-            pk[2 * kb + (v >> 3)][v & 7] = hp[0];
-            pk[2 * kb + (v >> 3)][(v & 7) + 1] = hp[1];
-            ls = __builtin_amdgcn_fdot2(hp, ones, ls, false);
-          }
-          if (i >= 1 && i <= 16) {
-            const int q = i - 1;
-            ea[q][0] = fast_exp2(xa[q][0]);
-            ea[q][1] = fast_exp2(xa[q][1]);
-          }
-          if (i < 16) {
-            const int kb = i >> 3, v = 2 * (i & 7);
-            xa[i][0] = fmaf(Sc[kb][v], c_log2, -mn);
-            xa[i][1] = fmaf(Sc[kb][v + 1], c_log2, -mn);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 18; ++i) {
+        if (i < 16) {
+          if (i + 3 < 16) kv[i + 3] = kread(i + 3);
+          Sn[i & 1] = mfma32x32x16(u4_to_h8(kv[i]), qreg[i >> 1], Sn[i & 1]);
         }
+        if (i >= 2) {
+          const int q = i - 2, kb = q >> 3, v = 2 * (q & 7);
+          const half2v hp = half2v{(_Float16)ea[q][0], (_Float16)ea[q][1]};
+          pk[2 * kb + (v >> 3)][v & 7] = hp[0];
+          pk[2 * kb + (v >> 3)][(v & 7) + 1] = hp[1];
+          ls = __builtin_amdgcn_fdot2(hp, ones, ls, false);
+        }
+        if (i >= 1 && i <= 16) {
+          const int q = i - 1;
+          ea[q][0] = fast_exp2(xa[q][0]);
+          ea[q][1] = fast_exp2(xa[q][1]);
+        }
+        if (i < 16) {
+          const int kb = i >> 3, v = 2 * (i & 7);
+          xa[i][0] = fmaf(Sc[kb][v], c_log2, -mn);
+          xa[i][1] = fmaf(Sc[kb][v + 1], c_log2, -mn);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // every weight is computed here (nothing of the block sinks into the
-      // rare branch below)
+      return ls;
+    };
+
+    // After the QK block: every weight is computed (nothing of the block
+    // sinks into the rare branch).  Rare: a lane's weight sum beyond the
+    // fp16-safe limit (a score more than ~15 above m in log2 units, or a row's
+    // first key after tiles that gave it none): the tile's scores are formed
+    // again from its K-hat stage (so the QK block need not keep them), masked,
+    // and m moved, the accumulator and normaliser rescaled and the weights
+    // recomputed.
+    auto settle_weights = [&](float ls) {
       asm volatile("" : "+v"(ls), "+v"(pk[0]), "+v"(pk[1]), "+v"(pk[2]), "+v"(pk[3]));
-      // Rare: a lane's weight sum beyond the fp16-safe limit (also every
-      // row's first tile, whose m starts at -1e30): take the row maximum,
-      // move m, rescale and recompute the weights.
       if (__builtin_amdgcn_ballot_w64(!(ls <= P_SUM_LIMIT)) != 0) {
-        asm volatile("" : "+v"(Sc[0]), "+v"(Sc[1]));   // keep this path in its branch
-        ls = rescale(Sc, pk);
+        asm volatile("" ::: "memory");   // the recompute stays inside this branch
+        f32x16 Sr[2];
+        qk_plain(kstage(jj & 3), Sr);
+        mask_tile(tj, kqj, Sr);
+        float alpha;
+        ls = rescale(Sr, pk, alpha);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] = o[db] * alpha;
       }
       l_run += ls;
+    };
 
-      // --- PV(j) interleaved with the dequantisation of tile j+2 ---
-      // MFMA i (i < 16): accumulator db = i % 4, k-step kk = i / 4.  Pair q
-      // of the staged tile (K pairs 0..7, then V pairs 0..7) goes through
-      // three slices: codes to biased fp16 in slice q, minus the biased
-      // zero-point in slice q + 1, times the scale in slice q + 2.
-      {
-        const uint8_t* vl = reinterpret_cast<const uint8_t*>(stage_at(j3)) + LDS_K;
-        auto vread = [&](int i) -> u32x4 {
-          const int db = i & 3, kk = i >> 2;
-          return *reinterpret_cast<const u32x4*>(vl + (32 * db + i32) * VS_STRIDE +
-                                                 (16 * kk + 8 * hb) * 2);
-        };
-        char* sdst = stage_at(ring_prev(j3));
-        const int unit = tid >> 1, khalf = tid & 1;
-        const int kkey = unit >> 2, kgrp = unit & 3;
-        const int vd = tid >> 2, vq = tid & 3;
-        const uint32_t knz = neg_biased_zero_h2(st.kz);
-        const _Float16 ksc = bits_to_half((uint16_t)st.ks);
-        const uint32_t ks2 = h2_to_u32(half2v{ksc, ksc});
-        u32x4 ko[2], vo[2];
-        u32x4 av[16];
-        uint32_t cb[16], cz[16], nzv[8];
+    // PV block: O^T += V-hat^T (tile j) P^T (pk), with the dequantisation of
+    // the staged tile (walk tile j+3) into its stages.  MFMA i
+    // (i < 16): accumulator db = i % 4, k-step kk = i / 4.  Pair q of the
+    // staged tile (K pairs 0..7, then V pairs 0..7) goes through three
+    // slices: codes to biased fp16 in slice q, minus the biased zero-point in
+    // slice q + 1, times the scale in slice q + 2.
+    auto pv_block = [&]() {
+      const uint8_t* vl = reinterpret_cast<const uint8_t*>(vstage(jj & 3));
+      auto vread = [&](int i) -> u32x4 {
+        const int db = i & 3, kk = i >> 2;
+        return *reinterpret_cast<const u32x4*>(vl + (32 * db + i32) * VS_STRIDE +
+                                               (16 * kk + 8 * hb) * 2);
+      };
+      char* kdst = kstage((jj + 3) & 3);
+      char* vdst = vstage((jj + 3) & 3);
+      const int unit = tid >> 1, khalf = tid & 1;
+      const int kkey = unit >> 2, kgrp = unit & 3;
+      const int vd = tid >> 2, vq = tid & 3;
+      const uint32_t knz = neg_biased_zero_h2(st.kz);
+      const _Float16 ksc = bits_to_half((uint16_t)st.ks);
+      const uint32_t ks2 = h2_to_u32(half2v{ksc, ksc});
+      u32x4 ko[2], vo[2];
+      u32x4 av[16];
+      uint32_t cb[16], cz[16], nzv[8];
 #pragma unroll
-        for (int i = 0; i < 3; ++i) av[i] = vread(i);
+      for (int i = 0; i < 3; ++i) av[i] = vread(i);
 #pragma unroll
-        for (int i = 0; i < 18; ++i) {
-          if (i < 16) {
-            if (i + 3 < 16) av[i + 3] = vread(i + 3);
-            o[i & 3] = mfma32x32x16(u4_to_h8(av[i]), pk[i >> 2], o[i & 3]);
-          }
-          if (i >= 2) {
-            const int q = i - 2;
-            if (q < 8) {
-              ko[q >> 2][q & 3] = h2_mul(cz[q], ks2);
-            } else {
-              const int jv = q - 8;
-              vo[vslot(jv) >> 2][vslot(jv) & 3] = h2_mul(cz[q], v_scales(st, jv));
-            }
-          }
-          if (i >= 1 && i <= 16) {
-            const int q = i - 1;
-            cz[q] = h2_add(cb[q], q < 8 ? knz : nzv[q - 8]);
-          }
-          if (i < 16) {
-            if (i < 8) {
-              cb[i] = k_biased<K8>(st, i);
-            } else {
-              cb[i] = v_biased<V8>(st, i - 8);
-              nzv[i - 8] = v_negzero(st, i - 8);
-            }
-          }
-          if (i == 10) {
-            u32x4* kd = reinterpret_cast<u32x4*>(sdst + kkey * KS_STRIDE + (32 * kgrp + 16 * khalf) * 2);
-            kd[0] = ko[0];
-            kd[1] = ko[1];
-          }
-          if (i == 17) {
-            u32x4* vdst = reinterpret_cast<u32x4*>(sdst + LDS_K + vd * VS_STRIDE + 32 * vq);
-            vdst[0] = vo[0];
-            vdst[1] = vo[1];
-          }
-          __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 18; ++i) {
+        if (i < 16) {
+          if (i + 3 < 16) av[i + 3] = vread(i + 3);
+          o[i & 3] = mfma32x32x16(u4_to_h8(av[i]), pk[i >> 2], o[i & 3]);
         }
+        if (i >= 2) {
+          const int q = i - 2;
+          if (q < 8) {
+            ko[q >> 2][q & 3] = h2_mul(cz[q], ks2);
+          } else {
+            const int jv2 = q - 8;
+            vo[vslot(jv2) >> 2][vslot(jv2) & 3] = h2_mul(cz[q], v_scales(st, jv2));
+          }
+        }
+        if (i >= 1 && i <= 16) {
+          const int q = i - 1;
+          cz[q] = h2_add(cb[q], q < 8 ? knz : nzv[q - 8]);
+        }
+        if (i < 16) {
+          if (i < 8) {
+            cb[i] = k_biased<K8>(st, i);
+          } else {
+            cb[i] = v_biased<V8>(st, i - 8);
+            nzv[i - 8] = v_negzero(st, i - 8);
+          }
+        }
+        if (i == 10) {
+          u32x4* kd = reinterpret_cast<u32x4*>(kdst + kkey * KS_STRIDE + (32 * kgrp + 16 * khalf) * 2);
+          kd[0] = ko[0];
+          kd[1] = ko[1];
+        }
+        if (i == 17) {
+          u32x4* vdp = reinterpret_cast<u32x4*>(vdst + vd * VS_STRIDE + 32 * vq);
+          vdp[0] = vo[0];
+          vdp[1] = vo[1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      stage_load<K8, V8>(rs, lo, (tj3 < nkt ? tj3 : t0_) * KT, st);
-      tj = tj1; tj1 = tj2; tj2 = tj3;
-      kqj = kqj1; kqj1 = kqj2; kqj2 = kqj3;
-      j3 = ring_next(j3);
+    };
+
+    auto iteration = [&](f32x16* Sc, f32x16* Sn) {
+      uint32_t kq5 = 7u;
+      const int tj5 = tj4 < nkt ? next_tile(tj4 + 1, kq5) : nkt;
+      if (!late) __syncthreads();
+      mask_tile(tj, kqj, Sc);
+      // the staged tile j+3: zero its V scales past the sequence end (rare)
+      const int tstaged = valid(tj3);
+      if (tstaged * KT + KT > n) {
+        asm volatile("" ::: "memory");
+        zero_tail_scales(st, tstaged * KT + 16 * (tid & 3), n);
+      }
+      settle_weights(qk_block(Sc, Sn));
+      if (late) __syncthreads();
+      pv_block();
+      stage_load<K8, V8>(rs, lo, valid(tj4) * KT, st);
+      tj = tj1; tj1 = tj2; tj2 = tj3; tj3 = tj4; tj4 = tj5;
+      kqj = kqj1; kqj1 = kqj2; kqj2 = kqj3; kqj3 = kqj4; kqj4 = kq5;
+      ++jj;
     };
 
     while (true) {
@@ -644,7 +709,7 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
 template <int R, bool K8, bool V8>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[NSTAGE * LDS_STAGE];
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
   const int H = a.nheads, B = a.k.B;
   const int id = blockIdx.x;
   const int g = a.heads[id % H];
