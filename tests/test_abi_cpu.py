@@ -49,10 +49,12 @@ def test_sizes():
     assert L.taq_kv_codes_bytes(ctypes.byref(cache())) == 2 * 256 * (128 + 64)
     assert L.taq_kv_meta_count(ctypes.byref(cache())) == 2 * 2 * 256 * 4
     assert L.taq_kv_codes_bytes(ctypes.byref(cache(bits=(3, 4)))) == 0
-    # decode workspace: B * Hq * nchunk * (D + 2) * 4
+    # decode workspace: partials B * Hq * nchunk * (D + 2) floats, then the
+    # chunk plan (a count, a pad word and B * Hkv * nchunk (unit, chunk) pairs);
+    # here B = 1 and Hkv = 2 give 128-token chunks (nchunk = 32)
     k = cache(B=1, H=2, cap=4096, bits=(8, 8))
     ws = L.taq_attn_decode_workspace_bytes(ctypes.byref(k), 8, 4096)
-    assert ws > 0 and ws % (130 * 4 * 8) == 0
+    assert ws == 1 * 8 * 32 * 130 * 4 + (2 + 2 * 1 * 2 * 32) * 4
 
 
 @pytest.mark.parametrize("kw,want", [

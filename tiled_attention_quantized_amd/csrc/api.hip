@@ -261,9 +261,7 @@ taq_status taq_kv_dequantize(const taq_kv_cache* c, int32_t start, int32_t count
 
 size_t taq_attn_decode_workspace_bytes(const taq_kv_cache* k, int32_t hq, int32_t max_len) {
   if (!k || k->batch < 1 || k->num_kv_heads < 1 || hq < 1 || max_len < 0) return 0;
-  const int chunk = taq::decode_chunk_tokens(k->batch, k->num_kv_heads, max_len);
-  const int64_t nchunk = max_len > 0 ? (max_len + chunk - 1) / chunk : 1;
-  return (size_t)k->batch * hq * nchunk * (128 + 2) * sizeof(float);
+  return taq::decode_workspace_bytes(k->batch, k->num_kv_heads, hq, max_len);
 }
 
 }  // extern "C"
@@ -621,8 +619,6 @@ SensPlan sens_plan(int B, int Hkv, int hq, int max_len) {
   p.cap = max_len > 0 ? (max_len + TAQ_TILE - 1) / TAQ_TILE * TAQ_TILE : TAQ_TILE;
   const size_t meta = (size_t)B * Hkv * p.cap * 4;
   const size_t c8 = (size_t)B * Hkv * p.cap * 128, c4 = c8 / 2;
-  const int chunk = taq::decode_chunk_tokens(B, Hkv, max_len);
-  const size_t nchunk = max_len > 0 ? (size_t)(max_len + chunk - 1) / chunk : 1;
   size_t at = 0;
   auto take = [&](size_t bytes) { const size_t o = at; at += align256(bytes); return o; };
   p.k8c = take(c8); p.k8s = take(2 * meta); p.k8z = take(meta);
@@ -631,7 +627,7 @@ SensPlan sens_plan(int B, int Hkv, int hq, int max_len) {
   p.v4c = take(c4); p.v4s = take(2 * meta); p.v4z = take(meta);
   p.o8 = take((size_t)B * hq * 128 * 2);
   p.o4 = take((size_t)B * hq * 128 * 2);
-  p.dec = take((size_t)B * hq * nchunk * (128 + 2) * sizeof(float));
+  p.dec = take(taq::decode_workspace_bytes(B, Hkv, hq, max_len));
   p.total = at;
   return p;
 }

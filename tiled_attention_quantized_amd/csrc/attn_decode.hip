@@ -10,7 +10,11 @@
 // Work decomposition (gfx950, wave64):
 //  * one workgroup per (KV chunk, KV head, batch); a 256-thread workgroup owns one chunk
 //    of `chunk` tokens of one (batch, KV head) and serves all r = Hq/Hkv query
-//    heads of that KV head, so each K/V byte is read once.
+//    heads of that KV head, so each K/V byte is read once.  Every precision
+//    variant runs in one launch; when the launch takes more than one round
+//    of workgroups, a one-workgroup plan kernel first lists the live chunks
+//    heaviest first (full 8-bit chunks down to the short last chunks of the
+//    sequences) and workgroup i takes entry i.
 //  * the 4 waves share the chunk in steps of 32 tokens (wave w takes step w of
 //    every 128-token tile) and each keeps its own (max, normaliser,
 //    accumulator).  The loads of the next steps are issued before the current
@@ -666,26 +670,105 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
   }
 }
 
+// Chunk plan: the live (unit, chunk) pairs of the call in the order the split
+// kernel's workgroups take them, heaviest first.  The weight of a chunk is
+// its 128-token tiles times the code bytes per token of its KV head (2, 3
+// or 4 units for int4/int4, mixed, int8/int8), so full chunks of 8-bit heads
+// come first and the short last chunks of the sequences fill the end of the
+// launch (the longest-job-first rule), and no workgroup slot goes to a chunk
+// past a sequence's end.  One workgroup: a histogram of the weights, a scan
+// from the heaviest weight down, then every item is placed at its weight's
+// next free position (the order inside one weight is immaterial: every
+// chunk's partial is computed and merged the same way wherever it runs).
+constexpr int PLAN_KEYS = 4 * 32 + 1;   // weights 0 .. 128
+
+__device__ __forceinline__ int chunk_cost(const DecodeArgs& a, int g) {
+  return (((a.k.is8 >> g) & 1ull) ? 2 : 1) + (((a.v.is8 >> g) & 1ull) ? 2 : 1);
+}
+
+__global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeArgs a) {
+  __shared__ int count[PLAN_KEYS];
+  __shared__ int next[PLAN_KEYS];
+  for (int i = threadIdx.x; i < PLAN_KEYS; i += blockDim.x) count[i] = 0;
+  __syncthreads();
+  const int H = a.k.H, units = a.k.B * H;
+  const int full_tiles = a.chunk / 128;
+  for (int u = threadIdx.x; u < units; u += blockDim.x) {
+    const int b = u / H, g = u - b * H;
+    int n = a.lens[b];
+    n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
+    const int cost = chunk_cost(a, g);
+    const int nfull = n / a.chunk, rem = n - nfull * a.chunk;
+    if (nfull > 0) atomicAdd(&count[full_tiles * cost], nfull);
+    if (rem > 0) atomicAdd(&count[((rem + 127) >> 7) * cost], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int at = 0;
+    for (int key = PLAN_KEYS - 1; key >= 0; --key) {
+      next[key] = at;
+      at += count[key];
+    }
+    a.plan[0] = (uint32_t)at;
+  }
+  __syncthreads();
+  uint2* items = reinterpret_cast<uint2*>(a.plan + 2);
+  for (int u = threadIdx.x; u < units; u += blockDim.x) {
+    const int b = u / H, g = u - b * H;
+    int n = a.lens[b];
+    n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
+    const int cost = chunk_cost(a, g);
+    const int nfull = n / a.chunk, rem = n - nfull * a.chunk;
+    for (int c = 0; c < nfull; ++c) {
+      const int at = atomicAdd(&next[full_tiles * cost], 1);
+      items[at] = make_uint2((uint32_t)u, (uint32_t)c);
+    }
+    if (rem > 0) {
+      const int at = atomicAdd(&next[((rem + 127) >> 7) * cost], 1);
+      items[at] = make_uint2((uint32_t)u, (uint32_t)nfull);
+    }
+  }
+}
+
 // Two waves per SIMD for every variant: the register budget that leaves
 // (up to 256 VGPRs) holds two steps of loads without spilling; at three waves
-// the int4 variant spilled and ran 20% slower.
-template <int R, bool K8, bool V8, int MODE>
+// the int4 variant spilled and ran 20% slower.  Workgroup i takes item i of
+// the plan (the grid covers every possible chunk; the rest return at once)
+// or, without a plan, chunk i % nchunk of unit i / nchunk,
+// and every (K bits, V bits) variant runs in this one launch, so heads of
+// different precision share the tail of the launch instead of each draining
+// the GPU.
+template <int R, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_split_kernel(DecodeArgs a) {
   __shared__ float lds[2 * WAVES * R + WAVES * R * D];
-  __shared__ __attribute__((aligned(16))) uint32_t vstage[WAVES * (V8 ? 1024 : 512)];
-  const int units = a.k.B * a.nheads;
-  // highest chunk index first: the later chunks exist only for the longest
-  // sequences, so they start early and the short final chunks fill the end
-  // (ragged lengths: 238 -> 235 us)
-  const int c = a.nchunk - 1 - (int)(blockIdx.x / units);
-  const int u = blockIdx.x - (a.nchunk - 1 - c) * units;
-  const int b = u / a.nheads;
-  const int g = a.heads[u - b * a.nheads];
+  __shared__ __attribute__((aligned(16))) uint32_t vstage[WAVES * 1024];
+  const int H = a.k.H;
+  int b, g, c;
+  if (a.plan != nullptr) {
+    if (blockIdx.x >= a.plan[0]) return;
+    const uint2 item = reinterpret_cast<const uint2*>(a.plan + 2)[blockIdx.x];
+    b = (int)item.x / H;
+    g = (int)item.x - b * H;
+    c = (int)item.y;
+  } else {
+    // one round of workgroups: the order is immaterial
+    const int u = blockIdx.x / a.nchunk;
+    c = blockIdx.x - u * a.nchunk;
+    b = u / H;
+    g = u - b * H;
+  }
   int n = a.lens[b];
   n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
   if (c * a.chunk >= n) return;
-  decode_body<R, K8, V8, MODE>(a, b, g, c, n, lds, vstage);
+  const bool k8 = ((a.k.is8 >> g) & 1ull) != 0, v8 = ((a.v.is8 >> g) & 1ull) != 0;
+  if (k8) {
+    if (v8) decode_body<R, true, true, MODE>(a, b, g, c, n, lds, vstage);
+    else decode_body<R, true, false, MODE>(a, b, g, c, n, lds, vstage);
+  } else {
+    if (v8) decode_body<R, false, true, MODE>(a, b, g, c, n, lds, vstage);
+    else decode_body<R, false, false, MODE>(a, b, g, c, n, lds, vstage);
+  }
 }
 
 // One workgroup per (batch, query head).  Every wave finds the global maximum
@@ -739,6 +822,18 @@ decode_merge_kernel(DecodeArgs a) {
 
 }  // namespace
 
+uint32_t* decode_plan_of(float* ws, int B, int Hq, int nchunk) {
+  return reinterpret_cast<uint32_t*>(ws + (int64_t)B * Hq * nchunk * (D + 2));
+}
+
+size_t decode_workspace_bytes(int B, int Hkv, int Hq, int max_len) {
+  const int chunk = decode_chunk_tokens(B, Hkv, max_len);
+  const int64_t nchunk = max_len > 0 ? (max_len + chunk - 1) / chunk : 1;
+  const size_t partials = (size_t)B * Hq * nchunk * (D + 2) * sizeof(float);
+  const size_t plan = (2 + 2 * (size_t)B * Hkv * nchunk) * sizeof(uint32_t);
+  return partials + plan;
+}
+
 int decode_chunk_tokens(int B, int Hkv, int max_len) {
   // Largest chunk (<= 4096 tokens) that still gives >= 2048 workgroups, so
   // every CU gets several; at least 128 (32 tokens per wave).
@@ -748,41 +843,30 @@ int decode_chunk_tokens(int B, int Hkv, int max_len) {
   return chunk;
 }
 
-template <int R, int MODE>
-hipError_t launch_variants(DecodeArgs a, hipStream_t s) {
-  // group the KV heads by their (K bits, V bits) variant
-  for (int var = 0; var < 4; ++var) {
-    const bool k8 = var & 2, v8 = var & 1;
-    a.nheads = 0;
-    for (int h = 0; h < a.k.H; ++h)
-      if ((((a.k.is8 >> h) & 1ull) != 0) == k8 && (((a.v.is8 >> h) & 1ull) != 0) == v8)
-        a.heads[a.nheads++] = (uint8_t)h;
-    if (a.nheads == 0) continue;
-    const dim3 grid(a.nchunk * a.nheads * a.k.B);
-    switch (var) {
-      case 0: hipLaunchKernelGGL((decode_split_kernel<R, false, false, MODE>), grid, dim3(256), 0, s, a); break;
-      case 1: hipLaunchKernelGGL((decode_split_kernel<R, false, true, MODE>), grid, dim3(256), 0, s, a); break;
-      case 2: hipLaunchKernelGGL((decode_split_kernel<R, true, false, MODE>), grid, dim3(256), 0, s, a); break;
-      default: hipLaunchKernelGGL((decode_split_kernel<R, true, true, MODE>), grid, dim3(256), 0, s, a); break;
-    }
+template <int MODE>
+hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.nchunk * a.k.H * a.k.B);
+  switch (a.r) {
+    case 1: hipLaunchKernelGGL((decode_split_kernel<1, MODE>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<2, MODE>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<4, MODE>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_split_kernel<8, MODE>), grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(const DecodeArgs& a_in, hipStream_t s, bool two_pass) {
+  DecodeArgs a = a_in;
+  // A launch that fits the GPU in one round of workgroups (two per CU) needs
+  // no plan; a longer one takes its chunks in the plan's order.
+  a.plan = nullptr;
+  if ((int64_t)a.nchunk * a.k.H * a.k.B > 512) {
+    a.plan = decode_plan_of(a.ws, a.k.B, a.Hq, a.nchunk);
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
-}
-
-template <int MODE>
-hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
-  switch (a.r) {
-    case 1: return launch_variants<1, MODE>(a, s);
-    case 2: return launch_variants<2, MODE>(a, s);
-    case 4: return launch_variants<4, MODE>(a, s);
-    case 8: return launch_variants<8, MODE>(a, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t s, bool two_pass) {
   hipError_t e;
   if (two_pass) {
     e = launch_split<MAX_PASS>(a, s);

@@ -36,11 +36,10 @@ struct DecodeArgs {
   const uint8_t* mask;   // null = none
   int64_t mask_sb, mask_sh;
   int32_t mask_nk;
-  float* ws;             // partials [B][Hq][nchunk][D + 2]
+  float* ws;             // partials [B][Hq][nchunk][D + 2], then the chunk plan
+  uint32_t* plan;        // [0]: live chunks; then (unit = b * Hkv + g, chunk) pairs
   int32_t Hq, r, max_len, chunk, nchunk;
   float scale_log2;      // softmax scale * log2(e)
-  int32_t nheads;        // KV heads handled by one launch, listed in heads[]
-  uint8_t heads[TAQ_MAX_KV_HEADS];
 };
 
 struct PrefillArgs {
@@ -89,5 +88,9 @@ int prefill_splits(int B, int Hkv, int r, int q_len, int max_len);
 
 // Decode split geometry chosen on the host (used for workspace sizing too).
 int decode_chunk_tokens(int B, int Hkv, int max_len);
+// Decode workspace: the chunk partials, then the chunk plan.
+size_t decode_workspace_bytes(int B, int Hkv, int Hq, int max_len);
+// The plan's place in a decode workspace.
+uint32_t* decode_plan_of(float* ws, int B, int Hq, int nchunk);
 
 }  // namespace taq
