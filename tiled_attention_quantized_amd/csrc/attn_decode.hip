@@ -748,6 +748,7 @@ decode_split_kernel(DecodeArgs a) {
   if (a.plan != nullptr) {
     if (blockIdx.x >= a.plan[0]) return;
     const uint2 item = reinterpret_cast<const uint2*>(a.plan + 2)[blockIdx.x];
+    if (item.x >= (uint32_t)(a.k.B * H) || item.y >= (uint32_t)a.nchunk) return;
     b = (int)item.x / H;
     g = (int)item.x - b * H;
     c = (int)item.y;
