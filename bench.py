@@ -443,21 +443,23 @@ def cpu_workers() -> int:
 
 
 def cpu_model() -> str:
-    """The host CPU's model name as lscpu reports it (else /proc/cpuinfo)."""
+    """The host CPU's model name: the longer of lscpu's "Model name" and
+    /proc/cpuinfo's "model name" (a virtual machine's lscpu may print only the
+    family)."""
     import subprocess
+    names = []
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
-        for ln in out.splitlines():
-            if ln.strip().startswith("Model name:"):
-                return ln.split(":", 1)[1].strip()
+        names += [ln.split(":", 1)[1].strip() for ln in out.splitlines()
+                  if ln.strip().startswith("Model name:")]
     except (OSError, subprocess.SubprocessError):
         pass
     try:
         with open("/proc/cpuinfo") as f:
-            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
-                        "")
+            names += [ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")][:1]
     except OSError:
-        return ""
+        pass
+    return max(names, key=len) if names else ""
 
 
 def cpu_baseline(inp, A):

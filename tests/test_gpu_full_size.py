@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import multiprocessing as mp
 import os
+import time
 from concurrent.futures import ProcessPoolExecutor
 
 import numpy as np
@@ -111,7 +112,10 @@ def test_decode_full_size_every_output(name):
     _G.clear()
     _G["inp"] = inp
     jobs = [(b, g) for b in range(spec.B) for g in range(spec.Hkv)]
+    t0 = time.perf_counter()
     res = _pool_map(_decode_job, jobs)
+    note(f"{name}: oracle {time.perf_counter() - t0:.1f} s on {min(_workers(), len(jobs))} "
+         f"host processes")
     r = spec.r
     err = 0.0
     for (b, g), want in zip(jobs, res):
@@ -157,7 +161,10 @@ def test_prefill_full_size(name):
     _G["inp"] = inp
     _G["rows"] = rows
     jobs = [(b, h) for b in range(spec.B) for h in range(spec.Hq)]
+    t0 = time.perf_counter()
     res = _pool_map(_prefill_job, jobs)
+    note(f"{name}: oracle {time.perf_counter() - t0:.1f} s on {min(_workers(), len(jobs))} "
+         f"host processes")
     err, worst = 0.0, None
     for (b, h), want in zip(jobs, res):
         d = np.abs(got[b, h] - want)
