@@ -6,7 +6,8 @@ element):
   element of the call;
 * prefill_128k_sparse (under its seeded 25% tile mask): every query head at
   every row of the first two and the last 128-row query tiles, plus rows
-  spread over the sequence.
+  spread over the sequence;
+* every workload's quantised K and V caches, dequantised: bit for bit.
 
 The oracle side is computed slab by slab (one batch entry and KV head, or one
 query head) in a forked process pool, so host memory stays bounded: each job
@@ -175,4 +176,49 @@ def test_prefill_full_size(name):
         assert e <= TOL, (name, b, h, e)
     note(f"{name}: {len(jobs)} heads x {rows.size} rows compared, max-abs {err:.3e} "
          f"at (b, h, row, channel, value) = {worst}")
+    _G.clear()
+
+
+def _dequant_job(args):
+    """Oracle quantise + dequantise of one (b, g) slab's token range, compared
+    bit for bit (fp32) with the GPU's dequantised values in _G."""
+    b, g, start, count, which = args
+    inp = _G["inp"]
+    x = (inp.k if which == "k" else inp.v)[b, g, start:start + count]
+    bits = int(inp.structure.head_bits[g])
+    want = oq.dequantize(*oq.quantize(x, bits)).astype(np.float32)
+    got = _G["got"][b, g]
+    same = np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    return same, int(np.count_nonzero(got.view(np.uint32) != want.view(np.uint32)))
+
+
+@pytest.mark.parametrize("name", ["decode_4k", "prefill_8k", "decode_ragged",
+                                  "decode_128k_mixed", "prefill_128k_sparse"])
+def test_quantize_full_size_bit_exact(name):
+    """kv_quantize of the workload's whole K and V (every token slot of the
+    capacity) dequantises, through kv_dequantize, to exactly the oracle's
+    fp32 values (quantise then dequantise, slab by slab)."""
+    require_gpu()
+    spec = W.WORKLOADS[name]
+    note(f"{name}: generating inputs")
+    inp = W.make_inputs(spec)
+    st = inp.structure
+    kc, vc = _gpu_caches(inp)
+    S = inp.k.shape[2]
+    chunk = 8192
+    _G.clear()
+    _G["inp"] = inp
+    for which, cache in (("k", kc), ("v", vc)):
+        for start in range(0, S, chunk):
+            count = min(chunk, S - start)
+            note(f"{name}: {which} tokens {start}..{start + count - 1}")
+            o32, _ = T.kv_dequantize(cache, start, count)
+            torch.cuda.synchronize()
+            _G["got"] = o32.cpu().numpy()
+            del o32
+            jobs = [(b, g, start, count, which) for b in range(spec.B) for g in range(spec.Hkv)]
+            res = _pool_map(_dequant_job, jobs)
+            bad = [(j, n) for j, (ok, n) in zip(jobs, res) if not ok]
+            assert not bad, (name, which, bad[:4])
+    note(f"{name}: K and V of {spec.B} x {spec.Hkv} slabs x {S} tokens dequantise bit for bit")
     _G.clear()
