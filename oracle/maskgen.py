@@ -29,7 +29,12 @@ that order as fp64 multiply then fp64 add (no fused multiply-add).
 Pins (tests/test_oracle_maskgen.py): exact drop counts per row, forced tiles,
 skip 0 = the dense causal mask, skip 1000 = first + diagonal only, a planted
 high-importance tile always kept, power-of-two rescaling invariance, and a
-pure-Python evaluation with Fractions on inputs without near-ties.
+pure-Python evaluation with Fractions on inputs without near-ties.  The
+per-turn variant (generate_chunk) is pinned by equality with generate() when
+the turn is the whole sequence and, for turns that start on a tile boundary,
+on the turn's rows; by its row structure and drop counts; and by a Fraction
+evaluation of a tile shared with the previous turn, whose ranking comes from
+the turn's rows alone.
 """
 from __future__ import annotations
 
@@ -80,6 +85,24 @@ def importance(qsum_row: np.ndarray, ksum: np.ndarray, cnt: np.ndarray) -> np.nd
     return s
 
 
+def _fill_row(row: np.ndarray, i: int, qsum_row, ksum, kcnt, skip_per_mille: int) -> None:
+    """Mask row of query tile i: tile 0 and the diagonal kept; of tiles
+    1 .. i-1 the floor((i-1) * skip / 1000) of lowest importance dropped
+    (ties: the lower j first), the rest kept."""
+    row[0] = 1
+    row[i] = 1
+    if i < 2:
+        return
+    js = np.arange(1, i)
+    m = (len(js) * skip_per_mille) // 1000
+    row[1:i] = 1
+    if m == 0:
+        return
+    s = importance(qsum_row, ksum[1:i], kcnt[1:i])
+    order = np.lexsort((js, s))          # by importance, then j
+    row[js[order[:m]]] = 0
+
+
 def generate(q, k_hat, seq_lens, skip_per_mille: int, max_seq_len: int | None = None):
     """Tile mask uint8 [B][Hkv][nt][nt], nt = ceil(max_seq_len / 128)
     (max_seq_len defaults to q's length)."""
@@ -95,16 +118,46 @@ def generate(q, k_hat, seq_lens, skip_per_mille: int, max_seq_len: int | None = 
         nt = (int(seq_lens[b]) + TILE - 1) // TILE
         for g in range(Hkv):
             for i in range(nt):
-                mask[b, g, i, 0] = 1
-                mask[b, g, i, i] = 1
-                if i < 2:
-                    continue
-                js = np.arange(1, i)
-                m = (len(js) * skip_per_mille) // 1000
-                mask[b, g, i, 1:i] = 1
-                if m == 0:
-                    continue
-                s = importance(qsum[b, g, i], ksum[b, g, 1:i], kcnt[b, 1:i])
-                order = np.lexsort((js, s))          # by importance, then j
-                mask[b, g, i, js[order[:m]]] = 0
+                _fill_row(mask[b, g, i], i, qsum[b, g, i], ksum[b, g], kcnt[b], skip_per_mille)
+    return mask
+
+
+def generate_chunk(q, k_hat, seq_lens, skip_per_mille: int, max_seq_len: int):
+    """Mask rows for one turn of a multi-turn prefill (section 4.2 of the
+    xdnf.cn page: a new turn reads the quantised history).  q fp16
+    [B][Hq][Lq][D] holds the last Lq positions of each sequence: row i of
+    batch entry b sits at position n_b - Lq + i (rows at negative positions
+    are padding), and the cache holds keys 0 .. n_b - 1 (the turn's own keys
+    included).  Reading taken: every query tile t that holds at least one of
+    the turn's positions gets the row generate() gives it, with Qsum_t the sum
+    of the turn's own rows in tile t (rows of earlier turns that share the
+    tile are not part of this call); every other row is 0.  Returns uint8
+    [B][Hkv][nt][nt], nt = ceil(max_seq_len / 128), indexed by positions as
+    the chunked prefill reads it."""
+    B, Hq, Lq, D = q.shape
+    Hkv = k_hat.shape[1]
+    if not 0 <= skip_per_mille <= 1000:
+        raise ValueError("skip_per_mille must lie in [0, 1000]")
+    if not 0 <= Lq <= max_seq_len:
+        raise ValueError("the turn's length must lie in [0, max_seq_len]")
+    nt_all = (max_seq_len + TILE - 1) // TILE
+    # the turn's rows at their positions: a tile's pooled sum then covers
+    # exactly the turn's rows in it
+    qpos = np.zeros((B, Hq, max_seq_len, D), dtype=np.float16)
+    for b in range(B):
+        n = int(seq_lens[b])
+        p0 = n - Lq
+        i0 = max(0, -p0)
+        if n > 0 and Lq > i0:
+            qpos[b, :, p0 + i0:n] = q[b, :, i0:]
+    qsum, ksum, kcnt = pooled(qpos, k_hat, seq_lens, Hkv)
+    mask = np.zeros((B, Hkv, nt_all, nt_all), dtype=np.uint8)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n <= 0 or Lq == 0:
+            continue
+        t_first, t_last = max(n - Lq, 0) // TILE, (n - 1) // TILE
+        for g in range(Hkv):
+            for i in range(t_first, t_last + 1):
+                _fill_row(mask[b, g, i], i, qsum[b, g, i], ksum[b, g], kcnt[b], skip_per_mille)
     return mask
