@@ -326,6 +326,27 @@ taq_status taq_tile_mask_generate(const taq_kv_cache* k_cache, const void* q_f16
                                   uint8_t* mask_out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* The same mask for one turn of a multi-turn prefill (section 4.2 of the
+ * xdnf.cn page: a new turn reads the quantised history), to drive
+ * taq_attn_prefill_chunk: q_f16 [B][Hq][q_len][128] holds the last q_len
+ * positions of each sequence (row i of entry b at position
+ * seq_lens[b] - q_len + i; rows at negative positions are padding and are not
+ * read), whose keys are already in k_cache.  Every query tile that holds one
+ * of the turn's positions gets the row taq_tile_mask_generate gives it, with
+ * Qsum summing the turn's own rows of that tile (the rows of an earlier turn
+ * that share the tile are not part of the call); every other row is written
+ * as 0 (chunked prefill reads only the turn's rows).  The mask is indexed by
+ * positions, in the layout and with the workspace of taq_tile_mask_generate
+ * for the same max_seq_len; q_len must lie in [0, max_seq_len] (q_f16 may be
+ * NULL when q_len is 0: every row is then 0); errors as
+ * taq_tile_mask_generate. */
+taq_status taq_tile_mask_generate_chunk(const taq_kv_cache* k_cache, const void* q_f16,
+                                        int32_t num_q_heads, int32_t q_len,
+                                        const int32_t* seq_lens, int32_t max_seq_len,
+                                        int32_t skip_per_mille, uint8_t* mask_out,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
 /* Workspace bytes that taq_head_sensitivity needs (0 for invalid sizes). */
 size_t taq_head_sensitivity_workspace_bytes(int32_t batch, int32_t num_kv_heads,
                                             int32_t num_q_heads, int32_t max_seq_len);

@@ -334,6 +334,34 @@ def test_tile_mask_rejects():
         assert maskgen_call(max_len=0)[0] == HIP
 
 
+def maskgen_chunk_call(k=None, hq=8, q_len=300, max_len=1000, spm=250, q=FAKE, lens=FAKE,
+                       out=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    k = k or cache(B=2, H=2, cap=1024, bits=(8, 4), layout=0)
+    return status_of(T.lib().taq_tile_mask_generate_chunk(ctypes.byref(k), q, hq, q_len, lens,
+                                                          max_len, spm, out, ws, ws_bytes, None))
+
+
+def test_tile_mask_chunk_rejects():
+    """The per-turn generator validates like the whole-prompt one, plus the
+    turn's length."""
+    assert maskgen_chunk_call(q_len=-1)[0] == INVALID
+    assert maskgen_chunk_call(q_len=1001)[0] == INVALID            # beyond max_seq_len
+    assert maskgen_chunk_call(hq=7)[0] == INVALID
+    assert maskgen_chunk_call(max_len=1025)[0] == INVALID
+    assert maskgen_chunk_call(spm=1001)[0] == INVALID
+    assert maskgen_chunk_call(q=0)[0] == INVALID
+    assert maskgen_chunk_call(q=FAKE + 2)[0] == MISALIGNED
+    assert maskgen_chunk_call(ws=0)[0] == WS_SMALL
+    assert maskgen_chunk_call(k=cache(B=2, H=2, cap=1024, bits=(8, 4), layout=1))[0] == UNSUPPORTED
+    assert maskgen_call(q=0)[0] == INVALID                          # a whole prompt needs q
+    if not os.path.exists("/dev/kfd"):
+        for ql in (0, 1, 300, 1000):
+            rc, msg = maskgen_chunk_call(q_len=ql)
+            assert rc == HIP, msg
+        rc, msg = maskgen_chunk_call(q_len=0, q=0)                 # an empty turn reads no q
+        assert rc == HIP, msg
+
+
 def sens_call(B=2, hkv=4, hq=8, max_len=300, n_high=1, k=FAKE, v=FAKE, q=FAKE, lens=FAKE,
               scores=FAKE, bits=FAKE, ws=FAKE, ws_bytes=1 << 40, scale=0.0):
     return status_of(T.lib().taq_head_sensitivity(k, v, q, B, hkv, hq, lens, max_len, scale,

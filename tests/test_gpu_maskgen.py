@@ -1,4 +1,5 @@
-"""GPU parity of the training-free tile-mask generator (taq_tile_mask_generate)
+"""GPU parity of the training-free tile-mask generator (taq_tile_mask_generate,
+and taq_tile_mask_generate_chunk for one turn of a multi-turn prefill)
 against the oracle's generator: the masks are compared byte for byte (the
 decision is taken in the same fp64 arithmetic on both sides), over ragged and
 empty sequences, mixed int4/int8 heads, several GQA ratios, every skip level
@@ -109,3 +110,59 @@ def test_generated_mask_drives_prefill(r):
     dense = oa.prefill(inp.q, k_hat, v_hat, lens, mask=None, rows=np.arange(896, 1000),
                        heads=[(0, 0)])
     assert max_abs(dense[0, 0], want[0, 0, 896:1000]) > 1e-2
+
+
+# ---- per-turn masks (taq_tile_mask_generate_chunk) ---------------------------
+
+@pytest.mark.parametrize("r,Lq,spm", [(1, 1, 500), (4, 100, 250), (4, 300, 600), (8, 1000, 250),
+                                      (2, 1000, 1000), (4, 0, 250)])
+def test_chunk_mask_equals_oracle(r, Lq, spm):
+    """Mask rows of one turn (the last Lq positions of ragged, empty and
+    short sequences; turns longer than a sequence carry padding rows) equal
+    the oracle's byte for byte."""
+    require_gpu()
+    Hkv = 2 if r < 8 else 1
+    lens = [1000, 333, 0, 129][: 4 if r < 8 else 3]
+    spec, inp, kc, k_hat, lens = _case(len(lens), Hkv * r, Hkv, 1000, lens,
+                                       n_int8=1 if Hkv == 2 else 0, seed=r * 11 + Lq)
+    qc = np.ascontiguousarray(inp.q[:, :, :Lq])      # the turn's queries (any fp16 data)
+    note(f"maskgen turn r={r} Lq={Lq} spm={spm} lens={lens.tolist()}")
+    tm = T.tile_mask_generate_chunk(kc, torch.from_numpy(qc).cuda(), lens_tensor(lens), 1000, spm)
+    torch.cuda.synchronize()
+    got = tm.data.cpu().numpy()
+    want = omg.generate_chunk(qc, k_hat, lens, spm, 1000)
+    _assert_mask_equal(got, want)
+
+
+@pytest.mark.parametrize("r,Lq", [(4, 300), (2, 700)])
+def test_chunk_mask_drives_chunked_prefill(r, Lq):
+    """A turn's generated mask drives taq_attn_prefill_chunk (key range split
+    over workgroups) within the bar of the oracle's chunked prefill under the
+    oracle's mask, and the mask drops tiles that change the result."""
+    require_gpu()
+    Hkv = 2
+    L = 1200
+    lens = [1200, 900]
+    spec, inp, kc, k_hat, lens = _case(2, Hkv * r, Hkv, L, lens, seed=201 + r)
+    hb = inp.structure.head_bits
+    vc = gpu_cache(inp.v, hb, T.LAYOUT_CHANNEL, spec.cap)
+    # the turn: the last Lq positions' queries of each sequence
+    qc = np.zeros((2, Hkv * r, Lq, 128), dtype=np.float16)
+    for b, n in enumerate(lens):
+        lo = n - Lq
+        qc[b, :, max(0, -lo):] = inp.q[b, :, max(lo, 0):n]
+    note(f"maskgen turn -> chunked prefill r={r} Lq={Lq}")
+    q = torch.from_numpy(qc).cuda()
+    lt = lens_tensor(lens)
+    tm = T.tile_mask_generate_chunk(kc, q, lt, L, 600)
+    out = T.attn_prefill_chunk(kc, vc, q, lt, L, mask=tm)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    mask = omg.generate_chunk(qc, k_hat, lens, 600, L)
+    assert np.array_equal(tm.data.cpu().numpy(), mask)
+    v_hat = oq.dequantized_all(oq.build_cache(inp.v, hb, "channel", cap=spec.cap))
+    want = oa.prefill_chunk(qc, k_hat, v_hat, lens, mask=mask, workers=4)
+    err = max_abs(got, want)
+    assert err <= TOL, err
+    dense = oa.prefill_chunk(qc, k_hat, v_hat, lens, mask=None, workers=4)
+    assert max_abs(dense, want) > 1e-2

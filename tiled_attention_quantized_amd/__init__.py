@@ -35,7 +35,7 @@ EXPORTS = ("taq_last_error", "taq_abi_version", "taq_device_check",
            "taq_tile_mask_generate", "taq_attn_decode_two_pass",
            "taq_head_sensitivity_workspace_bytes", "taq_head_sensitivity",
            "taq_attn_prefill_chunk_workspace_bytes", "taq_kv_quantize_pair",
-           "taq_attn_decode_noalloc")
+           "taq_attn_decode_noalloc", "taq_tile_mask_generate_chunk")
 
 
 class TaqError(RuntimeError):
@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
         "taq_head_sensitivity": (ctypes.c_int, [P, P, P, I32, I32, I32, P, I32, F, I32, P, P, P,
                                                 SZ, P]),
         "taq_tile_mask_generate": (ctypes.c_int, [CP, P, I32, P, I32, I32, P, P, SZ, P]),
+        "taq_tile_mask_generate_chunk": (ctypes.c_int, [CP, P, I32, I32, P, I32, I32, P, P, SZ,
+                                                         P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -354,6 +356,34 @@ def tile_mask_generate(k: KVCache, q, seq_lens, skip_per_mille: int, out=None, w
                                         int(skip_per_mille), _ptr(out), _ptr(workspace),
                                         workspace.numel() * workspace.element_size(),
                                         _stream(q.device)))
+    return TileMask(out, nt, nt, stride_b=k.num_kv_heads * nt * nt, stride_h=nt * nt)
+
+
+def tile_mask_generate_chunk(k: KVCache, q, seq_lens, max_seq_len: int, skip_per_mille: int,
+                             out=None, workspace=None):
+    """The KV-tile mask rows of one turn of a multi-turn prefill: q fp16
+    [B][Hq][q_len][D] holds the last q_len positions of each sequence (whose
+    keys are in `k`); returns a TileMask over uint8 [B][Hkv][nt][nt], nt =
+    ceil(max_seq_len / 128), indexed by positions (for attn_prefill_chunk)."""
+    import torch
+    if q.dtype != torch.float16 or not q.is_contiguous() or q.dim() != 4:
+        raise ValueError("q must be a contiguous fp16 [B][Hq][q_len][D] tensor")
+    B, Hq, Lq, D = q.shape
+    nt = (max_seq_len + 127) // 128
+    if out is None:
+        out = torch.empty((B, k.num_kv_heads, nt, nt), dtype=torch.uint8, device=q.device)
+    elif (out.dtype != torch.uint8 or not out.is_contiguous()
+          or tuple(out.shape) != (B, k.num_kv_heads, nt, nt)):
+        raise ValueError("out must be a contiguous uint8 [B][Hkv][nt][nt] tensor")
+    if workspace is None:
+        nb = tile_mask_workspace_bytes(k, max_seq_len)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)
+    kd = k.desc()
+    _check(lib().taq_tile_mask_generate_chunk(ctypes.byref(kd), _ptr(q), Hq, Lq, _ptr(seq_lens),
+                                              max_seq_len, int(skip_per_mille), _ptr(out),
+                                              _ptr(workspace),
+                                              workspace.numel() * workspace.element_size(),
+                                              _stream(q.device)))
     return TileMask(out, nt, nt, stride_b=k.num_kv_heads * nt * nt, stride_h=nt * nt)
 
 

@@ -545,10 +545,16 @@ size_t taq_tile_mask_workspace_bytes(const taq_kv_cache* k, int32_t max_len) {
   return (size_t)k->batch * k->num_kv_heads * nt * (2 * k->head_dim + nt) * sizeof(double);
 }
 
-taq_status taq_tile_mask_generate(const taq_kv_cache* k, const void* q, int32_t hq,
-                                  const int32_t* lens, int32_t max_len,
-                                  int32_t skip_per_mille, uint8_t* mask_out, void* ws,
-                                  size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of taq_tile_mask_generate (q_len = max_len, turn = false) and
+// taq_tile_mask_generate_chunk (q holds the last q_len positions).
+taq_status tile_mask_common(const taq_kv_cache* k, const void* q, int32_t hq, int32_t q_len,
+                            bool turn, const int32_t* lens, int32_t max_len,
+                            int32_t skip_per_mille, uint8_t* mask_out, void* ws,
+                            size_t ws_bytes, void* stream) {
   taq_status st = check_cache(k, "k_cache", TAQ_LAYOUT_TOKEN, true);
   if (st) return st;
   if (hq < 1 || hq % k->num_kv_heads)
@@ -560,6 +566,8 @@ taq_status taq_tile_mask_generate(const taq_kv_cache* k, const void* q, int32_t 
   if (max_len < 0 || max_len > k->capacity)
     return fail(TAQ_ERR_INVALID_ARGUMENT, "max_seq_len %d outside [0, capacity %d]", max_len,
                 k->capacity);
+  if (q_len < 0 || q_len > max_len)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "q_len %d outside [0, max_seq_len %d]", q_len, max_len);
   {
     const int64_t nt = (max_len + TAQ_TILE - 1) / TAQ_TILE, nb = (nt + 63) / 64;
     const int64_t bh = (int64_t)k->batch * k->num_kv_heads;
@@ -571,8 +579,10 @@ taq_status taq_tile_mask_generate(const taq_kv_cache* k, const void* q, int32_t 
                 taq::MASKGEN_MAX_TILES);
   if (skip_per_mille < 0 || skip_per_mille > 1000)
     return fail(TAQ_ERR_INVALID_ARGUMENT, "skip_per_mille %d outside [0, 1000]", skip_per_mille);
-  if (!q || !lens || !mask_out) return fail(TAQ_ERR_INVALID_ARGUMENT, "null q, seq_lens or mask");
-  if (!aligned16(q) || !aligned16(lens))
+  // an empty turn reads no query (q may be NULL)
+  if ((!q && q_len > 0) || !lens || !mask_out)
+    return fail(TAQ_ERR_INVALID_ARGUMENT, "null q, seq_lens or mask");
+  if ((q && !aligned16(q)) || !aligned16(lens))
     return fail(TAQ_ERR_MISALIGNED, "q and seq_lens must be 16-byte aligned");
   const size_t need = taq_tile_mask_workspace_bytes(k, max_len);
   if (!ws || ws_bytes < need)
@@ -595,9 +605,31 @@ taq_status taq_tile_mask_generate(const taq_kv_cache* k, const void* q, int32_t 
   a.Hq = hq;
   a.r = hq / k->num_kv_heads;
   a.L = max_len;
+  a.Lq = q_len;
+  a.turn = turn ? 1 : 0;
   a.skip_per_mille = skip_per_mille;
   hipError_t e = taq::launch_tile_mask(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TAQ_OK : hip_fail(e, "tile_mask launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+taq_status taq_tile_mask_generate(const taq_kv_cache* k, const void* q, int32_t hq,
+                                  const int32_t* lens, int32_t max_len,
+                                  int32_t skip_per_mille, uint8_t* mask_out, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  return tile_mask_common(k, q, hq, max_len, false, lens, max_len, skip_per_mille, mask_out, ws,
+                          ws_bytes, stream);
+}
+
+taq_status taq_tile_mask_generate_chunk(const taq_kv_cache* k, const void* q, int32_t hq,
+                                        int32_t q_len, const int32_t* lens, int32_t max_len,
+                                        int32_t skip_per_mille, uint8_t* mask_out, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  return tile_mask_common(k, q, hq, q_len, true, lens, max_len, skip_per_mille, mask_out, ws,
+                          ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -65,13 +65,16 @@ struct PrefillArgs {
 constexpr int MASKGEN_MAX_TILES = 2048;   // tiles per side (max_seq_len <= 262144)
 struct MaskGenArgs {
   CacheGeom k;
-  const uint16_t* q;     // [B][Hq][L][D]
+  const uint16_t* q;     // [B][Hq][Lq][D]; row i of entry b at position pos0_b + i
   const int32_t* lens;
   uint8_t* mask;         // [B][Hkv][nt][nt]
   double* qsum;          // workspace [B][Hkv][nt][D]: query sums in units of 2^-24
   double* kmean;         // workspace [B][Hkv][D][nt]: mean dequantised key per tile
   double* score;         // workspace [B][Hkv][nt][nt]: importance (lower triangle)
   int32_t Hq, r, L, nt, skip_per_mille;
+  int32_t Lq;            // rows of q (L for a whole prompt)
+  int32_t turn;          // nonzero: q is a turn, pos0_b = n_b - Lq, and only the
+                         // rows of the turn's query tiles are generated
 };
 hipError_t launch_tile_mask(const MaskGenArgs& a, hipStream_t s);
 

@@ -15,6 +15,11 @@
 // 2^-24), Kmean = double(Ksum) / cnt / 2^24, and the dot product runs over d
 // in order as a double multiply then a double add (no fused multiply-add).
 //
+// For one turn of a multi-turn prefill (q holds the last Lq positions of each
+// sequence, section 4.2 of the same page), the rows of the query tiles that
+// hold the turn's positions are generated, each ranked from the turn's own
+// rows in the tile; every other row is 0.
+//
 // Kernels: pool_q (one workgroup per (b, g, tile)), pool_k (same, reading the
 // quantised K cache), score (the lower triangle of Qsum . Kmean^T in 64 x 64
 // blocks), select (one wave per (b, g, query tile): the m lowest scores found
@@ -34,12 +39,12 @@ constexpr double UNIT = 16777216.0;   // 2^24
 constexpr int POOL_THREADS = 256;
 
 __device__ __forceinline__ void pool_unit(const MaskGenArgs& a, int& b, int& g, int& t,
-                                          int& lo, int& hi) {
+                                          int& lo, int& hi, int& n) {
   t = blockIdx.x % a.nt;
   const int rest = blockIdx.x / a.nt;
   g = rest % a.k.H;
   b = rest / a.k.H;
-  int n = a.lens[b];
+  n = a.lens[b];
   n = n < 0 ? 0 : (n > a.L ? a.L : n);
   lo = t * TILE;
   hi = min(lo + TILE, n);
@@ -53,13 +58,17 @@ __global__ void __launch_bounds__(POOL_THREADS)
 pool_q_kernel(MaskGenArgs a) {
   __shared__ double red[16][128];
   const int tid = threadIdx.x, c8 = tid & 15, kr = tid >> 4;
-  int b, g, t, lo, hi;
-  pool_unit(a, b, g, t, lo, hi);
+  int b, g, t, lo, hi, n;
+  pool_unit(a, b, g, t, lo, hi, n);
+  // a turn holds positions pos0 .. n-1 (q row = position - pos0): the tile's
+  // sum covers the turn's rows in it
+  const int pos0 = a.turn ? n - a.Lq : 0;
+  lo = max(lo, pos0);
   double acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
   for (int hl = 0; hl < a.r; ++hl) {
-    const uint16_t* qp = a.q + (((int64_t)b * a.Hq + g * a.r + hl) * a.L) * 128 + 8 * c8;
+    const uint16_t* qp = a.q + (((int64_t)b * a.Hq + g * a.r + hl) * a.Lq - pos0) * 128 + 8 * c8;
     for (int row = lo + kr; row < hi; row += 16) {
       // Q is read once here: non-temporal (keeps the caches for the K
       // pooling; 128K prompt: 451 -> 416 us for the whole generator)
@@ -96,8 +105,8 @@ __global__ void __launch_bounds__(POOL_THREADS)
 pool_k_kernel(MaskGenArgs a) {
   __shared__ long long red[16][128];
   const int tid = threadIdx.x, c8 = tid & 15, kr = tid >> 4;
-  int b, g, t, lo, hi;
-  pool_unit(a, b, g, t, lo, hi);
+  int b, g, t, lo, hi, n;
+  pool_unit(a, b, g, t, lo, hi, n);
   const bool is8 = (a.k.is8 >> g) & 1ull;
   const uint8_t* codes = a.k.codes + (int64_t)b * a.k.bstride + a.k.hoff[g];
   const int64_t mrow = ((int64_t)b * a.k.H + g) * a.k.cap * 4 + (c8 >> 2);
@@ -251,7 +260,9 @@ select_kernel(MaskGenArgs a) {
   int n = a.lens[b];
   n = n < 0 ? 0 : (n > a.L ? a.L : n);
   const int nt_b = (n + TILE - 1) / TILE;
-  const bool live = i < nt_b;
+  // a turn generates the rows of the query tiles that hold its positions
+  const int first = a.turn ? (a.Lq > 0 ? max(n - a.Lq, 0) / TILE : nt_b) : 0;
+  const bool live = i < nt_b && i >= first;
   const int ncand = i - 1;                       // tiles 1 .. i-1
   const int64_t bg = (int64_t)b * a.k.H + g;
   uint8_t* row = a.mask + (bg * a.nt + i) * a.nt;
