@@ -308,7 +308,9 @@ def bench_extras(which, torch, T, W, A):
     maskgen  tile_mask_generate (skip 250 per mille) on the 128K workload's Q
              and K;
     chunk    a 512-row chunk against 8192 cached tokens (Hq 32, Hkv 8, int8),
-             alone and with the two kv_append calls of the new tokens;
+             alone, with the two kv_append calls of the new tokens, and the
+             turn's own KV-tile mask (tile_mask_generate_chunk, skip 250 per
+             mille) alone and followed by the chunk under it;
     twopass  the long-context decode with the online softmax and with the
              literal two-pass softmax (same algorithmic bytes; pass 1 re-reads K);
     headbits per-KV-head sensitivity and precision assignment over the
@@ -411,10 +413,22 @@ def bench_extras(which, torch, T, W, A):
             T.kv_append(v, xv, starts)
             T.attn_prefill_chunk(k, v, q, lens, cap, out=out, workspace=ws)
         med2, _, _ = _median_ms(torch, with_append, 20)
+        # the turn's own KV-tile mask (skip 250 per mille), then the chunk under it
+        mws = torch.empty(T.tile_mask_workspace_bytes(k, cap), dtype=torch.uint8, device="cuda")
+        tm = T.tile_mask_generate_chunk(k, q, lens, cap, 250, workspace=mws)
+        med3, _, _ = _median_ms(torch, lambda: T.tile_mask_generate_chunk(
+            k, q, lens, cap, 250, out=tm.data, workspace=mws), 20)
+
+        def with_turn_mask():
+            T.tile_mask_generate_chunk(k, q, lens, cap, 250, out=tm.data, workspace=mws)
+            T.attn_prefill_chunk(k, v, q, lens, cap, mask=tm, out=out, workspace=ws)
+        med4, _, _ = _median_ms(torch, with_turn_mask, 20)
         tf = flops / (med * 1e-3) / 1e12
         print(json.dumps({"extra": "chunk", "workload": f"chunk {Lq} rows after {hist} cached",
                           "key_splits_workspace_bytes": int(nb),
                           "ms": round(med, 4), "ms_with_append": round(med2, 4),
+                          "ms_turn_mask": round(med3, 4),
+                          "ms_turn_mask_then_chunk": round(med4, 4),
                           "flops": int(flops), "TFLOP/s": round(tf, 1),
                           "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}), flush=True)
 
