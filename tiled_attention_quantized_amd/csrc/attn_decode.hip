@@ -274,7 +274,6 @@ __device__ __forceinline__ bool step_scores(const DecodeArgs& a, WaveState<R, K8
   float sc[NRB][2];
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk) {
-    const int tl = qk_token<V8>(bk, i16);
     const uint32_t nz = neg_biased_zero_h2(s.kz[bk]);
     half8 bk8[4];
     if (K8) {
