@@ -39,10 +39,11 @@
 //    recomputed (a rare branch that forms the tile's scores again).  The
 //    result is the same softmax: the factor exp2(-m) cancels between
 //    numerator and normaliser;
-//  * the needed tiles are found from scalar bit windows over 32 mask tiles
-//    (one vector load and ballot per window and query tile), and the
-//    causal / length / mask masking of a tile's scores only runs on tiles
-//    that need it;
+//  * the needed tiles are taken from 64-bit windows over 64 key tiles (one
+//    byte load per lane and query tile and three ballots per window; a tile
+//    is then a find-first-set and a clear), and the causal / length / mask
+//    masking of a tile's scores only runs on tiles that need it, one compare
+//    and select per score;
 //  * the workgroup order runs the longest causal rows first.
 #include "taq_internal.h"
 #include "device_common.h"
@@ -227,16 +228,6 @@ __device__ __forceinline__ void stage_store(const Staged& s, int tid, char* kdst
   vd[1] = vo[1];
 }
 
-// Keep bits of the 32 mask tiles w0 .. w0+31 for query tile qt: bit i set
-// when tile w0 + i lies at or below the diagonal (w0 + i <= qt) and the mask
-// keeps it (every such tile when there is no mask).  One byte load per lane.
-__device__ __forceinline__ uint32_t keep_window(const uint8_t* mrow, int qt, int w0, int lane) {
-  const int kt = w0 + (lane & 31);
-  bool keep = lane < 32 && kt <= qt;
-  if (mrow != nullptr && keep) keep = mrow[kt] != 0;
-  return (uint32_t)__builtin_amdgcn_ballot_w64(keep);
-}
-
 template <int R, bool K8, bool V8>
 __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int split, int n,
                              char* lds) {
@@ -296,58 +287,70 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
   const int qt_last = wg_last >= 0 ? (wg_last >> 7) : -1;
   const int nqt = min(qt_last - qt_first + 1, 3);
 
-  // ---- tile walk over scalar keep windows ----------------------------------
-  // win[i]: keep bits of query tile qt_first + i over mask tiles w0 .. w0+31;
-  // wgwin: their union (the tiles the workgroup needs).
-  int w0 = -32;
-  uint32_t win[3] = {0u, 0u, 0u};
-  uint32_t wgwin = 0u;
-  auto refill = [&](int base) {
-    w0 = base;
-    wgwin = 0u;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      win[i] = 0u;
-      if (i < nqt) {
-        const int qt = qt_first + i;
-        win[i] = keep_window(mb ? mb + (int64_t)qt * a.mask_nk : nullptr, qt, base, lane);
-        wgwin |= win[i];
-      }
-    }
-  };
-  // First needed 64-key tile at or after t (nkt if none), and its keep bits:
-  // bit i of kq set when query tile qt_first + i keeps it.  The bits travel
-  // with the tile (the window may move on before the tile is processed).
-  auto next_tile = [&](int t, uint32_t& kq) -> int {
-    kq = 7u;
-    if (mb == nullptr) return min(t, nkt);   // dense: every tile below nkt is needed
-    while (t < nkt) {
-      const int t128 = t >> 1;
-      if (t128 >= w0 + 32 || t128 < w0) refill(t128 & ~31);
-      const int sh = t128 - w0;
-      const uint32_t bits = wgwin >> sh;
-      if (bits & 1u) {
-        kq = ((win[0] >> sh) & 1u) | (((win[1] >> sh) & 1u) << 1) | (((win[2] >> sh) & 1u) << 2);
-        return t;
-      }
-      if (bits == 0u) {
-        t = 2 * (w0 + 32);
-      } else {
-        t = 2 * (t128 + __builtin_ctz(bits));
-      }
-    }
-    return nkt;
-  };
-  // query-tile indices (relative to qt_first) of the wave's first and last
-  // row, and of this lane's row
-  int qia, qib, qil;
+  // query tiles of the wave's first and last live row (a wave's 32 rows span
+  // at most two), and whether this lane's row lies in the first of them
+  int qia, qib;
+  bool lane_in_a;
   {
     const int qa = max(p0w, 0) >> 7, qb = max(min(p0w + 31, n - 1), 0) >> 7;
     qia = min(max(qa - qt_first, 0), 2);
     qib = min(max(qb - qt_first, 0), 2);
     const int ql = max(min(pos, n - 1), 0) >> 7;
-    qil = min(max(ql - qt_first, 0), 2);
+    lane_in_a = min(max(ql - qt_first, 0), 2) == qia;
   }
+
+  // ---- tile walk over 64-tile bit windows ------------------------------------
+  // Window [wb, wb + 64) of 64-key tiles, one bit per tile and lane of a
+  // ballot: U = tiles of [kt_lo, nkt) some query tile of the workgroup keeps
+  // and not yet taken; Wa / Wb = tiles the query tile of the wave's first /
+  // last row keeps (a query tile keeps a tile at or below its diagonal that
+  // the mask keeps; every tile of the range without a mask).
+  int wb = kt_lo & ~63;
+  uint64_t U = 0, Wa = 0, Wb = 0;
+  auto refill = [&]() {
+    const int kt = wb + lane;
+    const bool in = kt >= kt_lo && kt < nkt;
+    bool any = in, keep_a = in, keep_b = in;
+    if (mb != nullptr) {
+      // every lane loads (lanes past the range read the range's last mask
+      // tile), so the loads of all query tiles are in flight together
+      any = keep_a = keep_b = false;
+      const int mt = kt >> 1;
+      const int mtc = min(mt, (nkt - 1) >> 1);
+      uint32_t byte[3];
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        byte[i] = i < nqt ? mb[(int64_t)(qt_first + i) * a.mask_nk + mtc] : 0u;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const bool k = in && mt <= qt_first + i && byte[i] != 0u;
+        any |= k;
+        if (i == qia) keep_a = k;
+        if (i == qib) keep_b = k;
+      }
+    }
+    U = __builtin_amdgcn_ballot_w64(any);
+    Wa = __builtin_amdgcn_ballot_w64(keep_a);
+    Wb = __builtin_amdgcn_ballot_w64(keep_b);
+  };
+  // Next needed tile (nkt when the range is done) and its two keep bits
+  // (bit 0: the wave's first query tile keeps it, bit 1: its last); the bits
+  // travel with the tile, as the window may move on before it is processed.
+  auto pop = [&](uint32_t& kab) -> int {
+    kab = 3u;
+    while (U == 0) {
+      if (wb + 64 >= nkt) return nkt;
+      wb += 64;
+      refill();
+    }
+    const int i = __builtin_ctzll(U);
+    U &= U - 1;
+    kab = (uint32_t)((Wa >> i) & 1u) | ((uint32_t)((Wb >> i) & 1u) << 1);
+    return wb + i;
+  };
+  // First tile whose scores need the causal or length masking for some row
+  // of the wave (every tile when the wave holds padding rows).
+  const int t_crit = blk_dead ? -(1 << 30) : min(((p0w - (KT - 1)) >> 6) + 1, ((n - KT) >> 6) + 1);
 
   float m_run = NEG_BIG, l_run = 0.f;
   f32x16 o[4];
@@ -378,20 +381,24 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
   };
 
   // causal / length / dead-row / mask masking of tile t's scores (keep bits
-  // kq; only on tiles that need it)
-  auto mask_tile = [&](int t, uint32_t kq, f32x16* S) {
-    const int kt0 = t * KT;
-    const bool all_keep = ((kq >> qia) & (kq >> qib) & 1u) != 0u;
-    const bool need = (kt0 + KT - 1 > p0w) || (kt0 + KT > n) || blk_dead || !all_keep;
-    if (need) {
-      const bool keep = ((kq >> qil) & 1u) != 0u;
+  // kab; only on tiles that need it).  The lane's keys kt0 + 4 hb + off
+  // (off = 32 kb + 8 (v / 4) + v % 4) stay when off <= r, r from the row's
+  // last admitted key; each element is one compare into VCC and one select
+  // (kept as pairs, so the compares do not pile up in scalar registers).
+  auto mask_tile = [&](int t, uint32_t kab, f32x16* S) {
+    if (__builtin_amdgcn_readfirstlane((int)(t >= t_crit) | (int)(kab != 3u)) != 0) {
+      const bool keep = ((lane_in_a ? kab : kab >> 1) & 1u) != 0u;
+      const int last = (keep && row_live) ? min(pos, n - 1) : -(1 << 30);
+      const int r = last - t * KT - 4 * hb;
+      const float ninf = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kt0 + 32 * kb + 8 * (v >> 2) + 4 * hb + (v & 3);
-          if (!keep || key > pos || key >= n || !row_live) S[kb][v] = -INFINITY;
-        }
+        for (int v = 0; v < 16; ++v)
+          asm("v_cmp_gt_i32_e32 vcc, %2, %1\n\tv_cndmask_b32_e32 %0, %0, %3, vcc"
+              : "+v"(S[kb][v])
+              : "v"(r), "n"(32 * kb + 8 * (v >> 2) + (v & 3)), "v"(ninf)
+              : "vcc");
     }
   };
 
@@ -444,14 +451,15 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
   // dequantisation.  Every wave walks the same tiles; rows a tile does not
   // reach are masked, so the loop has no per-wave branches other than the
   // barrier's place.
-  uint32_t kq0, kq1 = 7u, kq2 = 7u, kq3 = 7u, kq4 = 7u;
-  const int t0_ = next_tile(kt_lo, kq0);
+  if (kt_lo < nkt) refill();
+  uint32_t kab0, kab1 = 3u, kab2 = 3u, kab3 = 3u, kab4 = 3u;
+  const int t0_ = pop(kab0);
   if (t0_ < nkt) {
     // tile window: walk tiles j .. j+4 (nkt past the end) and their keep bits
-    const int t1_ = next_tile(t0_ + 1, kq1);
-    const int t2_ = t1_ < nkt ? next_tile(t1_ + 1, kq2) : nkt;
-    const int t3_ = t2_ < nkt ? next_tile(t2_ + 1, kq3) : nkt;
-    const int t4_ = t3_ < nkt ? next_tile(t3_ + 1, kq4) : nkt;
+    const int t1_ = pop(kab1);
+    const int t2_ = t1_ < nkt ? pop(kab2) : nkt;
+    const int t3_ = t2_ < nkt ? pop(kab3) : nkt;
+    const int t4_ = t3_ < nkt ? pop(kab4) : nkt;
     // SIMD of each wave (hardware wave id register, SIMD field); a wave is
     // late when an earlier wave of the workgroup sits on the same SIMD
     int* simd_of = reinterpret_cast<int*>(lds + LDS_TABLE);
@@ -474,12 +482,12 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
       const int mine = simd_of[w];
       for (int u = 0; u < w; ++u) late_b |= simd_of[u] == mine;
     }
-    const bool late = __builtin_amdgcn_readfirstlane((int)late_b) != 0;
+    const int late = __builtin_amdgcn_readfirstlane((int)late_b);
 
     f32x16 S0[2], S1[2];
     qk_plain(kstage(0), S0);
     // m starts at the first tile's row maximum, so its weights need no rescale
-    mask_tile(t0_, kq0, S0);
+    mask_tile(t0_, kab0, S0);
     {
       float mx = S0[0][0];
 #pragma unroll
@@ -490,7 +498,8 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
       m_run = fmaxf(m_run, mx);   // a row with no key in the tile keeps NEG_BIG
     }
     int tj = t0_, tj1 = t1_, tj2 = t2_, tj3 = t3_, tj4 = t4_;
-    uint32_t kqj = kq0, kqj1 = kq1, kqj2 = kq2, kqj3 = kq3, kqj4 = kq4;
+    // keep bits of tiles j .. j+4, two per tile
+    uint32_t kabs = kab0 | (kab1 << 2) | (kab2 << 4) | (kab3 << 6) | (kab4 << 8);
     int jj = 0;   // walk index of tile j
     half8 pk[4];  // weights of tile j
 
@@ -561,7 +570,7 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
         asm volatile("" ::: "memory");   // the recompute stays inside this branch
         f32x16 Sr[2];
         qk_plain(kstage(jj & 3), Sr);
-        mask_tile(tj, kqj, Sr);
+        mask_tile(tj, kabs & 3u, Sr);
         float alpha;
         ls = rescale(Sr, pk, alpha);
 #pragma unroll
@@ -638,10 +647,10 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
     };
 
     auto iteration = [&](f32x16* Sc, f32x16* Sn) {
-      uint32_t kq5 = 7u;
-      const int tj5 = tj4 < nkt ? next_tile(tj4 + 1, kq5) : nkt;
-      if (!late) __syncthreads();
-      mask_tile(tj, kqj, Sc);
+      uint32_t kab5 = 3u;
+      const int tj5 = tj4 < nkt ? pop(kab5) : nkt;
+      if (late == 0) __syncthreads();
+      mask_tile(tj, kabs & 3u, Sc);
       // the staged tile j+3: zero its V scales past the sequence end (rare)
       const int tstaged = valid(tj3);
       if (tstaged * KT + KT > n) {
@@ -649,11 +658,11 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
         zero_tail_scales(st, tstaged * KT + 16 * (tid & 3), n);
       }
       settle_weights(qk_block(Sc, Sn));
-      if (late) __syncthreads();
+      if (late != 0) __syncthreads();
       pv_block();
       stage_load<K8, V8>(rs, lo, valid(tj4) * KT, st);
       tj = tj1; tj1 = tj2; tj2 = tj3; tj3 = tj4; tj4 = tj5;
-      kqj = kqj1; kqj1 = kqj2; kqj2 = kqj3; kqj3 = kqj4; kqj4 = kq5;
+      kabs = (kabs >> 2) | (kab5 << 8);
       ++jj;
     };
 
