@@ -101,27 +101,23 @@ struct Staged {
   u32x4 vs[2];     // V scales of the 16 keys
 };
 
-// Base addresses of one (batch, KV head) slab.  A tile load is a uniform
-// base (held in scalar registers) plus a uniform tile offset plus a fixed
-// 32-bit per-lane offset.  Every tile a workgroup loads lies below the
-// sequence length, so all loads stay inside the slab.
-struct Bases {
-  const uint8_t* k;
-  const uint8_t* kz;
-  const uint8_t* ks;
-  const uint8_t* v;
-  const uint8_t* vz;
-  const uint8_t* vs;
+// Buffer resources of one (batch, KV head) slab's six arrays.  A tile load
+// is then the resource, the tile's byte offset (a scalar operand of the
+// instruction) and a fixed per-lane byte offset: no address arithmetic per
+// tile beyond one shift per array.  Every tile a workgroup loads lies below
+// the sequence length, so all loads stay inside the slab (and a read past
+// a resource's size would return 0).
+struct Slab {
+  __amdgpu_buffer_rsrc_t k, kz, ks, v, vz, vs;
 };
 
-template <typename T>
-__device__ __forceinline__ T load_at(const uint8_t* base, uint32_t tile_off, uint32_t lane_off) {
-  return *reinterpret_cast<const T*>(base + tile_off + lane_off);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
 // Per-thread byte offsets of its share of a tile (from the tile's first key).
 struct LaneOff {
-  uint32_t k, km, v, vm;
+  uint32_t k, kz, ks, v, vz, vs;
 };
 
 template <bool K8, bool V8>
@@ -130,40 +126,37 @@ __device__ __forceinline__ LaneOff lane_offsets(int tid, int cap) {
   const int unit = tid >> 1, half = tid & 1;
   const int key = unit >> 2, grp = unit & 3;
   o.k = (uint32_t)(key * (K8 ? D : D / 2) + (K8 ? 32 : 16) * grp + (K8 ? 16 : 8) * half);
-  o.km = (uint32_t)(key * 4 + grp);
+  o.kz = (uint32_t)(key * 4 + grp);
+  o.ks = 2 * o.kz;
   const int d = tid >> 2, q = tid & 3;
   // key 16 q of the tile lies in 32-key block q / 2 at position 16 (q % 2)
   o.v = (uint32_t)(((q >> 1) * D + d) * (V8 ? 32 : 16) + (V8 ? 16 : 8) * (q & 1));
-  o.vm = (uint32_t)((d >> 5) * cap + 16 * q);
+  o.vz = (uint32_t)((d >> 5) * cap + 16 * q);
+  o.vs = 2 * o.vz;
   return o;
 }
 
 template <bool K8, bool V8>
-__device__ __forceinline__ void stage_load(const Bases& r, const LaneOff& o_in, int kt0, Staged& s) {
-  // The lane offsets are opaque here, so the compiler keeps each address as
-  // scalar base plus 32-bit lane offset instead of hoisting 64-bit per-lane
-  // pointers (two registers each) out of the tile loop.
-  LaneOff o = o_in;
-  asm volatile("" : "+v"(o.k), "+v"(o.km), "+v"(o.v), "+v"(o.vm));
-  const uint32_t tk = (uint32_t)kt0 * (K8 ? D : D / 2);
+__device__ __forceinline__ void stage_load(const Slab& r, const LaneOff& o, int kt0, Staged& s) {
+  const int tk = kt0 * (K8 ? D : D / 2);
   if (K8) {
-    s.kc = load_at<u32x4>(r.k, tk, o.k);
+    s.kc = __builtin_amdgcn_raw_buffer_load_b128(r.k, o.k, tk, 0);
   } else {
-    const u32x2 t = load_at<u32x2>(r.k, tk, o.k);
+    const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r.k, o.k, tk, 0);
     s.kc = u32x4{t[0], t[1], 0u, 0u};
   }
-  s.kz = load_at<uint8_t>(r.kz, (uint32_t)kt0 * 4, o.km);
-  s.ks = load_at<uint16_t>(r.ks, (uint32_t)kt0 * 8, 2 * o.km);
-  const uint32_t tv = (uint32_t)(kt0 >> 5) * D * (V8 ? 32 : 16);
+  s.kz = __builtin_amdgcn_raw_buffer_load_b8(r.kz, o.kz, kt0 * 4, 0);
+  s.ks = __builtin_amdgcn_raw_buffer_load_b16(r.ks, o.ks, kt0 * 8, 0);
+  const int tv = (kt0 >> 5) * D * (V8 ? 32 : 16);
   if (V8) {
-    s.vc = load_at<u32x4>(r.v, tv, o.v);
+    s.vc = __builtin_amdgcn_raw_buffer_load_b128(r.v, o.v, tv, 0);
   } else {
-    const u32x2 t = load_at<u32x2>(r.v, tv, o.v);
+    const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r.v, o.v, tv, 0);
     s.vc = u32x4{t[0], t[1], 0u, 0u};
   }
-  s.vz = load_at<u32x4>(r.vz, (uint32_t)kt0, o.vm);
-  s.vs[0] = load_at<u32x4>(r.vs, 2 * (uint32_t)kt0, 2 * o.vm);
-  s.vs[1] = load_at<u32x4>(r.vs, 2 * (uint32_t)kt0, 2 * o.vm + 16);
+  s.vz = __builtin_amdgcn_raw_buffer_load_b128(r.vz, o.vz, kt0, 0);
+  s.vs[0] = __builtin_amdgcn_raw_buffer_load_b128(r.vs, o.vs, 2 * kt0, 0);
+  s.vs[1] = __builtin_amdgcn_raw_buffer_load_b128(r.vs, o.vs + 16, 2 * kt0, 0);
 }
 
 // Dequantisation steps of one fp16 pair (K pair j in 0..7 = channels
@@ -251,13 +244,16 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
   // some row of the wave is padding (masked on every tile)
   const bool blk_dead = p0w < 0 || p0w + 31 >= n || q0w + 31 >= a.Lq;
 
-  Bases rs;
-  rs.k = a.k.codes + (int64_t)b * a.k.bstride + a.k.hoff[g];
-  rs.v = a.v.codes + (int64_t)b * a.v.bstride + a.v.hoff[g];
-  rs.ks = reinterpret_cast<const uint8_t*>(a.k.scales + ((int64_t)b * a.k.H + g) * a.k.cap * 4);
-  rs.kz = a.k.zeros + ((int64_t)b * a.k.H + g) * a.k.cap * 4;
-  rs.vs = reinterpret_cast<const uint8_t*>(a.v.scales + ((int64_t)b * a.v.H + g) * 4 * (int64_t)a.v.cap);
-  rs.vz = a.v.zeros + ((int64_t)b * a.v.H + g) * 4 * (int64_t)a.v.cap;
+  Slab rs;
+  {
+    const uint32_t cap = (uint32_t)a.k.cap;
+    rs.k = slab_rsrc(a.k.codes + (int64_t)b * a.k.bstride + a.k.hoff[g], cap * (K8 ? D : D / 2));
+    rs.v = slab_rsrc(a.v.codes + (int64_t)b * a.v.bstride + a.v.hoff[g], cap * (V8 ? D : D / 2));
+    rs.ks = slab_rsrc(a.k.scales + ((int64_t)b * a.k.H + g) * cap * 4, cap * 8);
+    rs.kz = slab_rsrc(a.k.zeros + ((int64_t)b * a.k.H + g) * cap * 4, cap * 4);
+    rs.vs = slab_rsrc(a.v.scales + ((int64_t)b * a.v.H + g) * 4 * (int64_t)cap, cap * 8);
+    rs.vz = slab_rsrc(a.v.zeros + ((int64_t)b * a.v.H + g) * 4 * (int64_t)cap, cap * 4);
+  }
   const LaneOff lo = lane_offsets<K8, V8>(tid, a.k.cap);
 
   const uint8_t* mb = a.mask ? a.mask + (int64_t)b * a.mask_sb + (int64_t)g * a.mask_sh : nullptr;
@@ -348,9 +344,11 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
     kab = (uint32_t)((Wa >> i) & 1u) | ((uint32_t)((Wb >> i) & 1u) << 1);
     return wb + i;
   };
-  // First tile whose scores need the causal or length masking for some row
-  // of the wave (every tile when the wave holds padding rows).
-  const int t_crit = blk_dead ? -(1 << 30) : min(((p0w - (KT - 1)) >> 6) + 1, ((n - KT) >> 6) + 1);
+  // First tile that reaches past the sequence end, and the first tile whose
+  // scores need the causal or length masking for some row of the wave
+  // (every tile when the wave holds padding rows).
+  const int t_len = ((n - KT) >> 6) + 1;
+  const int t_crit = blk_dead ? -(1 << 30) : min(((p0w - (KT - 1)) >> 6) + 1, t_len);
 
   float m_run = NEG_BIG, l_run = 0.f;
   f32x16 o[4];
@@ -386,7 +384,7 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
   // last admitted key; each element is one compare into VCC and one select
   // (kept as pairs, so the compares do not pile up in scalar registers).
   auto mask_tile = [&](int t, uint32_t kab, f32x16* S) {
-    if (__builtin_amdgcn_readfirstlane((int)(t >= t_crit) | (int)(kab != 3u)) != 0) {
+    if (((~(uint32_t)(t - t_crit) >> 31) | (kab ^ 3u)) != 0u) {
       const bool keep = ((lane_in_a ? kab : kab >> 1) & 1u) != 0u;
       const int last = (keep && row_live) ? min(pos, n - 1) : -(1 << 30);
       const int r = last - t * KT - 4 * hb;
@@ -648,12 +646,12 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
 
     auto iteration = [&](f32x16* Sc, f32x16* Sn) {
       uint32_t kab5 = 3u;
-      const int tj5 = tj4 < nkt ? pop(kab5) : nkt;
+      const int tj5 = pop(kab5);
       if (late == 0) __syncthreads();
       mask_tile(tj, kabs & 3u, Sc);
       // the staged tile j+3: zero its V scales past the sequence end (rare)
       const int tstaged = valid(tj3);
-      if (tstaged * KT + KT > n) {
+      if (tstaged >= t_len) {
         asm volatile("" ::: "memory");
         zero_tail_scales(st, tstaged * KT + 16 * (tid & 3), n);
       }
