@@ -498,7 +498,8 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
     int tj = t0_, tj1 = t1_, tj2 = t2_, tj3 = t3_, tj4 = t4_;
     // keep bits of tiles j .. j+4, two per tile
     uint32_t kabs = kab0 | (kab1 << 2) | (kab2 << 4) | (kab3 << 6) | (kab4 << 8);
-    int jj = 0;   // walk index of tile j
+    // the loop is unrolled four times, so tile j's ring stage (j % 4, the
+    // phase ph below) is a constant in each copy
     half8 pk[4];  // weights of tile j
 
     // QK block: S^T of tile j+1 into Sn, the weights of tile j (scores Sc)
@@ -509,9 +510,9 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
     // it: the exponent argument in slice q, the exponential in slice q + 1,
     // the fp16 rounding and the row sum in slice q + 2.  Past the last tile
     // the MFMAs recompute a resident stage (result unused).
-    auto qk_block = [&](const f32x16* Sc, f32x16* Sn) -> float {
+    auto qk_block = [&](int ph, const f32x16* Sc, f32x16* Sn) -> float {
       float ls = 0.f;
-      const uint8_t* kl = reinterpret_cast<const uint8_t*>(kstage((jj + 1) & 3));
+      const uint8_t* kl = reinterpret_cast<const uint8_t*>(kstage((ph + 1) & 3));
       auto kread = [&](int i) -> u32x4 {
         const int kb = i & 1, ks = i >> 1;
         return *reinterpret_cast<const u32x4*>(kl + (32 * kb + i32) * KS_STRIDE +
@@ -562,12 +563,12 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
     // again from its K-hat stage (so the QK block need not keep them), masked,
     // and m moved, the accumulator and normaliser rescaled and the weights
     // recomputed.
-    auto settle_weights = [&](float ls) {
+    auto settle_weights = [&](int ph, float ls) {
       asm volatile("" : "+v"(ls), "+v"(pk[0]), "+v"(pk[1]), "+v"(pk[2]), "+v"(pk[3]));
       if (__builtin_amdgcn_ballot_w64(!(ls <= P_SUM_LIMIT)) != 0) {
         asm volatile("" ::: "memory");   // the recompute stays inside this branch
         f32x16 Sr[2];
-        qk_plain(kstage(jj & 3), Sr);
+        qk_plain(kstage(ph), Sr);
         mask_tile(tj, kabs & 3u, Sr);
         float alpha;
         ls = rescale(Sr, pk, alpha);
@@ -583,15 +584,15 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
     // staged tile (K pairs 0..7, then V pairs 0..7) goes through three
     // slices: codes to biased fp16 in slice q, minus the biased zero-point in
     // slice q + 1, times the scale in slice q + 2.
-    auto pv_block = [&]() {
-      const uint8_t* vl = reinterpret_cast<const uint8_t*>(vstage(jj & 3));
+    auto pv_block = [&](int ph) {
+      const uint8_t* vl = reinterpret_cast<const uint8_t*>(vstage(ph));
       auto vread = [&](int i) -> u32x4 {
         const int db = i & 3, kk = i >> 2;
         return *reinterpret_cast<const u32x4*>(vl + (32 * db + i32) * VS_STRIDE +
                                                (16 * kk + 8 * hb) * 2);
       };
-      char* kdst = kstage((jj + 3) & 3);
-      char* vdst = vstage((jj + 3) & 3);
+      char* kdst = kstage((ph + 3) & 3);
+      char* vdst = vstage((ph + 3) & 3);
       const int unit = tid >> 1, khalf = tid & 1;
       const int kkey = unit >> 2, kgrp = unit & 3;
       const int vd = tid >> 2, vq = tid & 3;
@@ -644,7 +645,7 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
       }
     };
 
-    auto iteration = [&](f32x16* Sc, f32x16* Sn) {
+    auto iteration = [&](int ph, f32x16* Sc, f32x16* Sn) {
       uint32_t kab5 = 3u;
       const int tj5 = pop(kab5);
       if (late == 0) __syncthreads();
@@ -655,19 +656,22 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
         asm volatile("" ::: "memory");
         zero_tail_scales(st, tstaged * KT + 16 * (tid & 3), n);
       }
-      settle_weights(qk_block(Sc, Sn));
+      settle_weights(ph, qk_block(ph, Sc, Sn));
       if (late != 0) __syncthreads();
-      pv_block();
+      pv_block(ph);
       stage_load<K8, V8>(rs, lo, valid(tj4) * KT, st);
       tj = tj1; tj1 = tj2; tj2 = tj3; tj3 = tj4; tj4 = tj5;
       kabs = (kabs >> 2) | (kab5 << 8);
-      ++jj;
     };
 
     while (true) {
-      iteration(S0, S1);
+      iteration(0, S0, S1);
       if (tj >= nkt) break;
-      iteration(S1, S0);
+      iteration(1, S1, S0);
+      if (tj >= nkt) break;
+      iteration(2, S0, S1);
+      if (tj >= nkt) break;
+      iteration(3, S1, S0);
       if (tj >= nkt) break;
     }
   }
