@@ -505,7 +505,7 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
     // QK block: S^T of tile j+1 into Sn, the weights of tile j (scores Sc)
     // into pk; returns the lane's sum of the weights.  MFMA i (i < 16):
     // accumulator kb = i % 2, k-step ks = i / 2; its LDS operand is read
-    // three MFMAs ahead.  The weights of pair q (elements 2q, 2q+1 of S(j))
+    // two MFMAs ahead.  The weights of pair q (elements 2q, 2q+1 of S(j))
     // go through three slices so that no instruction waits on the one before
     // it: the exponent argument in slice q, the exponential in slice q + 1,
     // the fp16 rounding and the row sum in slice q + 2.  Past the last tile
@@ -527,11 +527,11 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
       u32x4 kv[16];
       float xa[16][2], ea[16][2];
 #pragma unroll
-      for (int i = 0; i < 3; ++i) kv[i] = kread(i);
+      for (int i = 0; i < 2; ++i) kv[i] = kread(i);
 #pragma unroll
       for (int i = 0; i < 18; ++i) {
         if (i < 16) {
-          if (i + 3 < 16) kv[i + 3] = kread(i + 3);
+          if (i + 2 < 16) kv[i + 2] = kread(i + 2);
           Sn[i & 1] = mfma32x32x16(u4_to_h8(kv[i]), qreg[i >> 1], Sn[i & 1]);
         }
         if (i >= 2) {
@@ -580,7 +580,9 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
 
     // PV block: O^T += V-hat^T (tile j) P^T (pk), with the dequantisation of
     // the staged tile (walk tile j+3) into its stages.  MFMA i
-    // (i < 16): accumulator db = i % 4, k-step kk = i / 4.  Pair q of the
+    // (i < 16): accumulator db = i % 4, k-step kk = i / 4; its LDS operand
+    // is read four MFMAs ahead (the QK block, whose slices are longer, reads
+    // two ahead: the depths that timed best).  Pair q of the
     // staged tile (K pairs 0..7, then V pairs 0..7) goes through three
     // slices: codes to biased fp16 in slice q, minus the biased zero-point in
     // slice q + 1, times the scale in slice q + 2.
@@ -603,11 +605,11 @@ __device__ void prefill_body(const PrefillArgs& a, int b, int g, int qblk, int s
       u32x4 av[16];
       uint32_t cb[16], cz[16], nzv[8];
 #pragma unroll
-      for (int i = 0; i < 3; ++i) av[i] = vread(i);
+      for (int i = 0; i < 4; ++i) av[i] = vread(i);
 #pragma unroll
       for (int i = 0; i < 18; ++i) {
         if (i < 16) {
-          if (i + 3 < 16) av[i + 3] = vread(i + 3);
+          if (i + 4 < 16) av[i + 4] = vread(i + 4);
           o[i & 3] = mfma32x32x16(u4_to_h8(av[i]), pk[i >> 2], o[i & 3]);
         }
         if (i >= 2) {
