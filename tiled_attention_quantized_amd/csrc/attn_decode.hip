@@ -31,8 +31,11 @@
 //
 // Per step, both contractions run on the matrix cores (v_mfma_f32_16x16x32_f16):
 //  * scores: A = block-diagonal Q (row = (head, quant group), 16 rows per block
-//    of 4 heads), B = K codes converted exactly to (c - z) in fp16.  Each lane
-//    ends up with the 4 per-group partial dot products of one (head, token) and
+//    of 4 heads), B = K codes as exact biased fp16 values (bias + c); one
+//    more MFMA per 16 tokens takes sum_c q_c (bias_c + z) off (from per-row
+//    sums of Q held as fp16 hi + lo pairs: exact products, fp32 sums), so no
+//    per-code zero-point add is needed.  Each lane ends
+//    up with the 4 per-group partial dot products of one (head, token) and
 //    applies the 4 group scales itself: score = sum_g s_g * dot_g.
 //  * PV: A = V-hat^T (rows = channels) dequantised to fp16 in registers from
 //    the channel-major V layout (8 consecutive tokens of one channel per lane;
@@ -223,6 +226,7 @@ template <int R, bool K8, bool V8>
 struct WaveState {
   static constexpr int NRB = (R + 3) / 4;
   half8 aq[NRB][4];
+  half8 az[NRB];   // zero-point operand: (Qs_hi, Qs_lo, X_hi, X_lo, 0, 0, 0, 0)
   float m_run[NRB], l_run[NRB];
   f32x4 acc[8];
 };
@@ -274,8 +278,11 @@ __device__ __forceinline__ bool step_scores(const DecodeArgs& a, WaveState<R, K8
   float sc[NRB][2];
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk) {
+    // B operands: the codes as exact biased fp16 values (bias + c), and
+    // zb = (-(1024 + z), -(1024 + z), 1, 1) for the zero-point MFMA (see az)
     const uint32_t nz = neg_biased_zero_h2(s.kz[bk]);
     half8 bk8[4];
+    const half8 zb = u4_to_h8(u32x4{nz, 0x3C003C00u, 0u, 0u});
     if (K8) {
       const uint32_t wv[8] = {s.kc[bk][0][0], s.kc[bk][0][1], s.kc[bk][0][2], s.kc[bk][0][3],
                               s.kc[bk][1][0], s.kc[bk][1][1], s.kc[bk][1][2], s.kc[bk][1][3]};
@@ -284,22 +291,19 @@ __device__ __forceinline__ bool step_scores(const DecodeArgs& a, WaveState<R, K8
         u32x4 o;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint32_t h2 = bytes_to_biased_h2(wv[2 * kk + (k >> 1)], k & 1);
-          o[k] = h2_to_u32(u32_to_h2(h2) + u32_to_h2(nz));
+          o[k] = bytes_to_biased_h2(wv[2 * kk + (k >> 1)], k & 1);
         }
         bk8[kk] = u4_to_h8(o);
       }
     } else {
       const u32x4 cw = s.kc[bk][0];
-      const uint32_t nzo = odd_nibble_negz(nz);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         u32x4 o;
         const uint32_t cws = cw[kk] >> 8;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint32_t h2 = nibbles_to_biased_h2(cw[kk], cws, k);
-          o[k] = h2_to_u32(u32_to_h2(h2) + u32_to_h2((k & 1) ? nzo : nz));
+          o[k] = nibbles_to_biased_h2(cw[kk], cws, k);
         }
         bk8[kk] = u4_to_h8(o);
       }
@@ -309,7 +313,7 @@ __device__ __forceinline__ bool step_scores(const DecodeArgs& a, WaveState<R, K8
     const float s2 = (float)u32_to_h2(sraw[1])[0], s3 = (float)u32_to_h2(sraw[1])[1];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      f32x4 d4 = {0.f, 0.f, 0.f, 0.f};
+      f32x4 d4 = mfma16x16x32(ws.az[rb], zb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) d4 = mfma16x16x32(ws.aq[rb][kk], bk8[kk], d4);
       float x = s0 * d4[0];
@@ -494,6 +498,27 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
       }
       ws.aq[rb][kk] = u4_to_h8(o);
     }
+    // Zero-point operand of the lane's (head, group) row.  The scores' B
+    // operand holds the codes with the bias of their slot (1024, or 64 for
+    // the odd int4 pairs), so a row's dot needs sum_c q_c (bias_c + z) taken
+    // off: -(1024 + z) Qs + X with Qs = sum_c q_c and X = 960 * (q of the
+    // odd int4 pairs).  One MFMA with B = (-(1024 + z), -(1024 + z), 1, 1)
+    // per token does it; Qs and X go in as fp16 hi + lo pairs, so the
+    // products are exact and the sums fp32.
+    float qs = 0.f, xo = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = (float)ws.aq[rb][kk][j];
+        qs += v;
+        if (!K8 && ((j >> 1) & 1)) xo += v;
+      }
+    xo *= 960.f;
+    const _Float16 qh = (_Float16)qs, xh = (_Float16)xo;
+    const _Float16 ql = (_Float16)(qs - (float)qh), xl = (_Float16)(xo - (float)xh);
+    const _Float16 z0 = (_Float16)0.f;
+    ws.az[rb] = half8{qh, ql, xh, xl, z0, z0, z0, z0};
   }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) { ws.m_run[rb] = NEG_BIG; ws.l_run[rb] = 0.f; }
