@@ -701,9 +701,9 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
 // come first and the short last chunks of the sequences fill the end of the
 // launch (the longest-job-first rule), and no workgroup slot goes to a chunk
 // past a sequence's end.  One workgroup: a histogram of the weights, a scan
-// from the heaviest weight down, then every item is placed at its weight's
-// next free position (the order inside one weight is immaterial: every
-// chunk's partial is computed and merged the same way wherever it runs).
+// from the heaviest weight down, then every unit reserves its chunks' slots
+// at its weights' next free positions (the order inside one weight is
+// immaterial: every chunk's partial is computed and merged the same way wherever it runs).
 constexpr int PLAN_KEYS = 4 * 32 + 1;   // weights 0 .. 128
 
 __device__ __forceinline__ int chunk_cost(const DecodeArgs& a, int g) {
@@ -743,9 +743,12 @@ __global__ void __launch_bounds__(1024) decode_plan_kernel(DecodeArgs a) {
     n = n < 0 ? 0 : (n > a.max_len ? a.max_len : n);
     const int cost = chunk_cost(a, g);
     const int nfull = n / a.chunk, rem = n - nfull * a.chunk;
-    for (int c = 0; c < nfull; ++c) {
-      const int at = atomicAdd(&next[full_tiles * cost], 1);
-      items[at] = make_uint2((uint32_t)u, (uint32_t)c);
+    if (nfull > 0) {
+      // one reservation for the unit's full chunks (same weight), not one
+      // atomic per chunk: the threads' reservations of one weight would
+      // otherwise serialise on its counter chunk by chunk
+      const int at = atomicAdd(&next[full_tiles * cost], nfull);
+      for (int c = 0; c < nfull; ++c) items[at + c] = make_uint2((uint32_t)u, (uint32_t)c);
     }
     if (rem > 0) {
       const int at = atomicAdd(&next[((rem + 127) >> 7) * cost], 1);
