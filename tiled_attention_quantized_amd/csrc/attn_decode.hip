@@ -703,7 +703,8 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
 // past a sequence's end.  One workgroup: a histogram of the weights, a scan
 // from the heaviest weight down, then every unit reserves its chunks' slots
 // at its weights' next free positions (the order inside one weight is
-// immaterial: every chunk's partial is computed and merged the same way wherever it runs).
+// immaterial: every chunk's partial is computed and merged the same way
+// wherever it runs).
 constexpr int PLAN_KEYS = 4 * 32 + 1;   // weights 0 .. 128
 
 __device__ __forceinline__ int chunk_cost(const DecodeArgs& a, int g) {
