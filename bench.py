@@ -436,14 +436,13 @@ def bench_extras(which, torch, T, W, A):
 # ---- CPU baseline --------------------------------------------------------------------
 
 def sample_rows(L: int, n: int = 4096):
-    """Rows of the oracle sample: evenly spaced over the sequence, plus its last
-    row (so the sample spans short and full-length causal rows).  The oracle
+    """Rows of the oracle sample: n rows evenly spaced over the sequence, its
+    first and last row included (so the sample spans short and full-length
+    causal rows).  The oracle
     scores blocks of 256 rows against every key, so its time grows with the
     number of row blocks: 4096 rows of the 128K workload take ~17 s on 16 host
     cores (plus ~5 s to quantise and dequantise the cache)."""
-    rows = set(int(x) for x in np.linspace(0, L - 1, n - 1).round())
-    rows.add(L - 1)
-    return np.array(sorted(rows))
+    return np.unique(np.linspace(0, L - 1, n).round().astype(np.int64))
 
 
 def cpu_workers() -> int:
