@@ -113,6 +113,40 @@ def test_prefill_masked(r):
     assert not got[1, :, 512:].any()
 
 
+@pytest.mark.parametrize("r", [4, 1])
+def test_prefill_mask_long_dropped_runs(r):
+    """A mask whose kept tiles are far apart: the query tiles of the second
+    half keep only tile 0, the diagonal and tiles next to the boundaries of
+    64-key-tile windows (mask tiles 31, 32, 63, 64, ...), so the tile walk
+    crosses windows with no kept tile at all, and rows of one wave can fall on
+    both sides of a query-tile boundary with different keep bits (r = 1: 256-row
+    query blocks).  Two entries, the second shorter (ragged tail in a dropped
+    run).  Sampled rows of every head against the oracle."""
+    require_gpu()
+    L = 16384
+    nt = L // 128
+    spec = W.small("prefill", B=2, Hq=2 * r, Hkv=2, L=L, bits=8, seed=31 + r)
+    inp = W.make_inputs(spec)
+    lens = np.array([L, L - 200], dtype=np.int32)
+    mask = np.tril(np.ones((nt, nt), dtype=np.uint8))
+    for qi in range(nt // 2, nt):
+        keep = {0, qi} | {k for k in (31, 32, 63, 64, 95, 96) if k <= qi}
+        if qi % 3 == 0:
+            keep.add(qi - 1)        # neighbour rows of a wave differ in this tile
+        mask[qi, :] = 0
+        mask[qi, sorted(keep)] = 1
+    masks = np.stack([mask, mask])
+    rows = np.unique(np.concatenate([np.arange(0, 130), np.arange(L // 2 - 130, L // 2 + 130),
+                                     np.linspace(L // 2, L - 1, 64).round().astype(int),
+                                     np.arange(L - 300, L)]))
+    note(f"prefill mask long dropped runs r={r} rows={rows.size}")
+    got, _ = gpu_run_np(inp, mask=masks, lens=lens)
+    want = oracle_run(inp, mask=masks, lens=lens, rows=rows, workers=8)
+    err = max_abs(got[:, :, rows], want)
+    assert err <= TOL, err
+    assert not got[1, :, lens[1]:].any()
+
+
 def test_prefill_uniform_v_and_determinism():
     require_gpu()
     spec = W.small("prefill", B=1, Hq=4, Hkv=1, L=300, bits=8, seed=21)
