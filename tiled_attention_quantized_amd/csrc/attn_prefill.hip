@@ -18,7 +18,9 @@
 //    rings of four stages as a software pipeline with one barrier per tile:
 //    the QK^T MFMAs of tile j+1 interleave with the weights of tile j, and
 //    the PV MFMAs of tile j with the dequantisation of tile j+3; tile j+4 is
-//    fetched into registers.  The two waves of a SIMD take the barrier at
+//    fetched into registers (buffer loads whose scalar offset is the tile's
+//    byte offset).  The loop is unrolled four times, so every ring stage is a
+//    constant LDS offset.  The two waves of a SIMD take the barrier at
 //    different points of that sequence, so while one computes exponentials
 //    the other dequantises.  Inside those blocks each chain of dependent
 //    vector instructions (exponent argument, exponential, fp16 rounding and
