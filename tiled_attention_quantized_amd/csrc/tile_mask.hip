@@ -142,22 +142,28 @@ pool_k_kernel(MaskGenArgs a) {
 }
 
 // Scores over the lower triangle in 64 x 64 blocks of (query tile i, KV tile
-// j): thread (ti, tj) of 256 owns i = I0 + ti + 16a and j = J0 + tj + 16c
-// (a, c < 4).  Qsum and Kmean pass through LDS 32 channels at a time; every
-// score is still accumulated over d = 0 .. 127 in order, multiply then add.
+// j), the blocks of the triangle only (block t of a head is the t-th
+// (bi, bj) with bj <= bi, row by row).  Thread (ti, tj) of 256 owns
+// i = I0 + 4 ti + x and j = J0 + 4 tj + y (x, y < 4).  Qsum and Kmean pass
+// through LDS 32 channels at a time, a thread's 4 rows (columns) contiguous
+// (two 16-byte reads each); every score is still accumulated over
+// d = 0 .. 127 in order, multiply then add.
 constexpr int SB = 64, SD = 32;
 
 __global__ void __launch_bounds__(256)
 score_kernel(MaskGenArgs a, int nb) {
 #pragma clang fp contract(off)
-  __shared__ double qs[SB][SD + 1];
-  __shared__ double ks[SD][SB];
-  const int bj = blockIdx.x % nb;
-  int rest = blockIdx.x / nb;
-  const int bi = rest % nb;
-  rest /= nb;
+  __shared__ __attribute__((aligned(16))) double qs[SD][SB];   // [e][row]
+  __shared__ __attribute__((aligned(16))) double ks[SD][SB];   // [e][column]
+  const int ntri = nb * (nb + 1) / 2;
+  const int t = blockIdx.x % ntri;
+  const int rest = blockIdx.x / ntri;
   const int g = rest % a.k.H, b = rest / a.k.H;
-  if (bj > bi) return;                          // whole workgroup, before any barrier
+  // row bi of the triangle holds blocks bi (bi + 1) / 2 .. + bi
+  int bi = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
+  while (bi * (bi + 1) / 2 > t) --bi;
+  while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
+  const int bj = t - bi * (bi + 1) / 2;
   const int I0 = bi * SB, J0 = bj * SB;
   const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
   const int64_t bg = (int64_t)b * a.k.H + g;
@@ -171,7 +177,7 @@ score_kernel(MaskGenArgs a, int nb) {
   for (int d0 = 0; d0 < 128; d0 += SD) {
     for (int x = tid; x < SB * SD; x += 256) {
       const int r = x / SD, e = x % SD, i = I0 + r;
-      qs[r][e] = i < a.nt ? qsum[(int64_t)i * 128 + d0 + e] : 0.0;
+      qs[e][r] = i < a.nt ? qsum[(int64_t)i * 128 + d0 + e] : 0.0;
     }
     for (int x = tid; x < SD * SB; x += 256) {
       const int e = x / SB, c = x % SB, j = J0 + c;
@@ -181,9 +187,9 @@ score_kernel(MaskGenArgs a, int nb) {
     for (int e = 0; e < SD; ++e) {
       double qv[4], kv[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) qv[x] = qs[ti + 16 * x][e];
+      for (int x = 0; x < 4; ++x) qv[x] = qs[e][4 * ti + x];
 #pragma unroll
-      for (int y = 0; y < 4; ++y) kv[y] = ks[e][tj + 16 * y];
+      for (int y = 0; y < 4; ++y) kv[y] = ks[e][4 * tj + y];
 #pragma unroll
       for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -196,7 +202,7 @@ score_kernel(MaskGenArgs a, int nb) {
   for (int x = 0; x < 4; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
-      const int i = I0 + ti + 16 * x, j = J0 + tj + 16 * y;
+      const int i = I0 + 4 * ti + x, j = J0 + 4 * tj + y;
       if (i < a.nt && j < i) S[(int64_t)i * a.nt + j] = acc[x][y];
     }
 }
@@ -296,8 +302,8 @@ hipError_t launch_tile_mask(const MaskGenArgs& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nb = (a.nt + SB - 1) / SB;
-  hipLaunchKernelGGL(score_kernel, dim3((unsigned)(a.k.B * a.k.H * nb * nb)), dim3(256), 0, s,
-                     a, nb);
+  hipLaunchKernelGGL(score_kernel, dim3((unsigned)(a.k.B * a.k.H * (nb * (nb + 1) / 2))),
+                     dim3(256), 0, s, a, nb);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned rows4 = (unsigned)(a.k.B * a.k.H * ((a.nt + 3) / 4));
