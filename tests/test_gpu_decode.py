@@ -183,6 +183,31 @@ def test_decode_deterministic():
                               got.astype(np.float16).view(np.uint16))
 
 
+@pytest.mark.parametrize("bits,n8", [(4, 0), (4, 1), (8, 0)])
+@pytest.mark.parametrize("kind", ["x12", "one_channel_20000"])
+def test_decode_large_query_magnitudes(bits, n8, kind):
+    """Queries far from unit scale: every channel x12 (group sums of the odd
+    int4 pairs reach ~1e5, beyond fp16), or one channel at 20000 (near the
+    fp16 range).  The scores take the zero-points off through per-row query
+    sums, which must stay exact and finite for any fp16 query; outputs match
+    the oracle within the bar."""
+    require_gpu()
+    spec = W.small("decode", B=2, Hq=8, Hkv=2, ragged=(300, 700), bits=bits,
+                   n_int8_heads=n8, seed=47)
+    inp = W.make_inputs(spec)
+    q = inp.q.astype(np.float32)
+    if kind == "x12":
+        q *= 12
+    else:
+        q[:, :, 5] = 20000.0
+    inp.q = q.astype(np.float16)
+    assert np.isfinite(inp.q).all()
+    note(f"decode large q {kind} bits={bits} n8={n8}")
+    got, want, _ = run_decode(inp)
+    assert np.isfinite(got).all()
+    assert max_abs(got, want) <= TOL
+
+
 def test_decode_error_scales_with_v_magnitude():
     """The 2e-3 bar is for unit-variance data.  V-hat enters the PV product as
     fp16, so its rounding error is relative: a V channel scaled by 2^4 keeps

@@ -226,7 +226,8 @@ template <int R, bool K8, bool V8>
 struct WaveState {
   static constexpr int NRB = (R + 3) / 4;
   half8 aq[NRB][4];
-  half8 az[NRB];   // zero-point operand: (Qs_hi, Qs_lo, X_hi, X_lo, 0, 0, 0, 0)
+  half8 az[NRB];       // zero-point operand (A): (Qs hi, lo, Qo hi, lo, 0, 0, 0, 0) / 2^e
+  uint32_t zneg, zodd;  // zero-point operand (B): fp16 -2^e (1024 + z) byte, 960 * 2^e pair
   float m_run[NRB], l_run[NRB];
   f32x4 acc[8];
 };
@@ -279,10 +280,12 @@ __device__ __forceinline__ bool step_scores(const DecodeArgs& a, WaveState<R, K8
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk) {
     // B operands: the codes as exact biased fp16 values (bias + c), and
-    // zb = (-(1024 + z), -(1024 + z), 1, 1) for the zero-point MFMA (see az)
-    const uint32_t nz = neg_biased_zero_h2(s.kz[bk]);
+    // zb = (-2^e (1024 + z), -2^e (1024 + z), 960 * 2^e, 960 * 2^e) for the
+    // zero-point MFMA (see az); -2^e (1024 + z) is the fp16 bit pattern
+    // (ws.zneg byte) << 8 | z
+    const uint32_t nz = perm_b32(ws.zneg, s.kz[bk], 0x04000400u);
     half8 bk8[4];
-    const half8 zb = u4_to_h8(u32x4{nz, 0x3C003C00u, 0u, 0u});
+    const half8 zb = u4_to_h8(u32x4{nz, ws.zodd, 0u, 0u});
     if (K8) {
       const uint32_t wv[8] = {s.kc[bk][0][0], s.kc[bk][0][1], s.kc[bk][0][2], s.kc[bk][0][3],
                               s.kc[bk][1][0], s.kc[bk][1][1], s.kc[bk][1][2], s.kc[bk][1][3]};
@@ -498,27 +501,47 @@ __device__ void decode_body(const DecodeArgs& a, int b, int g, int c, int n, flo
       }
       ws.aq[rb][kk] = u4_to_h8(o);
     }
-    // Zero-point operand of the lane's (head, group) row.  The scores' B
-    // operand holds the codes with the bias of their slot (1024, or 64 for
-    // the odd int4 pairs), so a row's dot needs sum_c q_c (bias_c + z) taken
-    // off: -(1024 + z) Qs + X with Qs = sum_c q_c and X = 960 * (q of the
-    // odd int4 pairs).  One MFMA with B = (-(1024 + z), -(1024 + z), 1, 1)
-    // per token does it; Qs and X go in as fp16 hi + lo pairs, so the
-    // products are exact and the sums fp32.
-    float qs = 0.f, xo = 0.f;
+  }
+  // Zero-point operand of each lane's (head, group) row.  The scores' B
+  // operand holds the codes with the bias of their slot (1024, or 64 for the
+  // odd int4 pairs), so a row's dot needs sum_c q_c (bias_c + z) taken off:
+  // -(1024 + z) Qs + 960 Qo, with Qs = sum_c q_c and Qo the sum over the odd
+  // int4 pairs.  One MFMA per 16 tokens does it, with
+  // A = (Qs hi, Qs lo, Qo hi, Qo lo) / 2^e and
+  // B = (-2^e (1024 + z), -2^e (1024 + z), 960 * 2^e, 960 * 2^e): the
+  // products are exact in fp32 and the sums fp32.  e = 0 unless a sum of the
+  // wave would leave the fp16 range (then e = 5, so that |Qs| / 32 and
+  // |Qo| / 32 are fp16 values for any fp16 query; e = 0 keeps the lo parts
+  // out of the fp16 subnormals for small sums).
+  {
+    float qs[NRB], qo[NRB];
+    bool big = false;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int rb = 0; rb < NRB; ++rb) {
+      qs[rb] = 0.f;
+      qo[rb] = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = (float)ws.aq[rb][kk][j];
-        qs += v;
-        if (!K8 && ((j >> 1) & 1)) xo += v;
-      }
-    xo *= 960.f;
-    const _Float16 qh = (_Float16)qs, xh = (_Float16)xo;
-    const _Float16 ql = (_Float16)(qs - (float)qh), xl = (_Float16)(xo - (float)xh);
-    const _Float16 z0 = (_Float16)0.f;
-    ws.az[rb] = half8{qh, ql, xh, xl, z0, z0, z0, z0};
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float v = (float)ws.aq[rb][kk][j];
+          qs[rb] += v;
+          if (!K8 && ((j >> 1) & 1)) qo[rb] += v;
+        }
+      big |= !(fabsf(qs[rb]) <= 32768.f && fabsf(qo[rb]) <= 32768.f);
+    }
+    const bool wave_big = __builtin_amdgcn_ballot_w64(big) != 0;
+    const float sc = wave_big ? 1.f / 32.f : 1.f;
+    ws.zneg = vconst(wave_big ? 0xF8F8F8F8u : 0xE4E4E4E4u);   // -(1024 + z) * 32 or * 1
+    ws.zodd = wave_big ? 0x73807380u : 0x63806380u;   // 15360 or 960
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float s2 = qs[rb] * sc, o2 = qo[rb] * sc;
+      const _Float16 qh = (_Float16)s2, oh = (_Float16)o2;
+      const _Float16 ql = (_Float16)(s2 - (float)qh), ol = (_Float16)(o2 - (float)oh);
+      const _Float16 z0 = (_Float16)0.f;
+      ws.az[rb] = half8{qh, ql, oh, ol, z0, z0, z0, z0};
+    }
   }
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) { ws.m_run[rb] = NEG_BIG; ws.l_run[rb] = 0.f; }
