@@ -147,6 +147,75 @@ def test_prefill_mask_long_dropped_runs(r):
     assert not got[1, :, lens[1]:].any()
 
 
+def _planted_inputs(r, q_scale, seed, low_start=0, n_high=0):
+    """Prefill inputs (L = 900, two KV heads) with queries scaled by q_scale.
+    The first low_start keys of each KV head are set to -40 times the unit
+    mean-query direction of the head (every row's first tile then scores far
+    below its later keys, so the running maximum has to move), and n_high
+    keys late in the sequence to +40 times it (scores far above the rest)."""
+    L = 900
+    spec = W.small("prefill", B=1, Hq=2 * r, Hkv=2, L=L, bits=8, seed=seed)
+    inp = W.make_inputs(spec)
+    q = inp.q.astype(np.float32) * q_scale
+    k = inp.k.astype(np.float32)
+    rng = np.random.default_rng(seed)
+    for g in range(2):
+        qd = q[0, g * r:(g + 1) * r].mean(axis=(0, 1))
+        qd /= np.linalg.norm(qd) + 1e-6
+        k[0, g, :low_start] = -40.0 * qd
+        for pos in rng.choice(np.arange(500, L), size=n_high, replace=False):
+            k[0, g, pos] = 40.0 * qd
+    inp.q = q.astype(np.float16)
+    inp.k = k.astype(np.float16)
+    nt = (L + 127) // 128
+    mask = np.tril(np.ones((nt, nt), dtype=np.uint8))
+    mask[5, 1:5] = 0         # rows of query tile 5 see only tile 0 and their own tile
+    return inp, mask
+
+
+@pytest.mark.parametrize("r", [4, 1])
+def test_prefill_rescale_path(r):
+    """Unit-scale queries whose first tile (keys set against the query
+    direction) scores more than 15 (log2 units) below later keys: the kernel
+    starts the running maximum at the first tile's row maximum, so its rare
+    branch (re-form the tile's scores, move the maximum, rescale the
+    accumulator and normaliser) runs for those rows.  The first tile's keys
+    end with weights ~2^-15 or less, so their larger K-hat rounding does not
+    reach the outputs.  Against the oracle within the bar."""
+    require_gpu()
+    inp, mask = _planted_inputs(r, 1.0, seed=61 + r, low_start=64)
+    okc = oq.build_cache(inp.k, inp.structure.head_bits, "token", cap=inp.spec.cap)
+    kh = oq.dequantized_all(okc)[0]
+    qs = inp.q[0].astype(np.float64)
+    jumps = 0
+    for h in range(2 * r):
+        s = qs[h] @ kh[h // r, :900].T / np.sqrt(128) / np.log(2)    # log2 units
+        s = np.where(np.tril(np.ones((900, 900), dtype=bool)), s, -np.inf)
+        first = s[:, :64].max(axis=1)
+        jumps += int(((s.max(axis=1) - first) > 15)[64:].sum())
+    assert jumps > 0                    # the rare branch is taken somewhere
+    note(f"prefill rescale path r={r} rows={jumps}")
+    got, _ = gpu_run_np(inp, mask=mask)
+    want = oracle_run(inp, mask=mask)
+    assert np.isfinite(got).all()
+    assert max_abs(got, want) <= TOL
+
+
+def test_prefill_large_scores_error_scales():
+    """Queries x10 (scores up to ~70 in log2 units) and a dozen planted keys:
+    K-hat enters the QK product as fp16, so the score error grows with the
+    score magnitude; the bar is for unit-scale queries, and ten times the
+    queries stay within ten times the bar (the output and V-hat rounding do
+    not grow).  Outputs stay finite through many rescales."""
+    require_gpu()
+    inp, mask = _planted_inputs(4, 10.0, seed=65, n_high=12)
+    note("prefill large scores")
+    got, _ = gpu_run_np(inp, mask=mask)
+    want = oracle_run(inp, mask=mask)
+    assert np.isfinite(got).all()
+    assert max_abs(got, want) <= 10 * TOL
+
+
 def test_prefill_uniform_v_and_determinism():
     require_gpu()
     spec = W.small("prefill", B=1, Hq=4, Hkv=1, L=300, bits=8, seed=21)
