@@ -252,8 +252,9 @@ taq_status taq_attn_decode_noalloc(const taq_kv_cache* k_cache,
  * page; tiles dropped by the block mask (its section 2.3) contribute nothing,
  * and query-row tiles whose whole KV range is skipped cost nothing.  The
  * dequantised K and V tiles enter the products as fp16 (the rounded exact
- * values), so the score error grows with |q| * |k| (unit-scale data stays
- * within 2e-3 of exact fp64 attention).  Same cache requirements as decode;
+ * values), so the score error grows with softmax_scale * |q| * |k|
+ * (unit-scale data at softmax_scale <= 1/sqrt(128) stays within 2e-3 of
+ * exact fp64 attention).  Same cache requirements as decode;
  * mask n_q_tiles and n_k_tiles must both cover ceil(max_seq_len / 128). */
 taq_status taq_attn_prefill(const taq_kv_cache* k_cache,
                             const taq_kv_cache* v_cache, const void* q_f16,

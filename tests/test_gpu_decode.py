@@ -14,7 +14,7 @@ from tests.gpu_util import (TOL, require_gpu, note, gpu_cache, max_abs, lens_ten
 pytestmark = pytest.mark.gpu
 
 
-def run_decode(inp, mask=None, heads=None, workers=4):
+def run_decode(inp, mask=None, heads=None, workers=4, scale=None):
     spec, st = inp.spec, inp.structure
     bits = st.head_bits
     kc = gpu_cache(inp.k, bits, T.LAYOUT_TOKEN, spec.cap)
@@ -25,14 +25,15 @@ def run_decode(inp, mask=None, heads=None, workers=4):
     if mask is not None:
         md = torch.from_numpy(np.ascontiguousarray(mask)).cuda()
         tm = T.TileMask(md, 1, mask.shape[-1], stride_b=mask.shape[-1] if mask.ndim == 2 else 0)
-    out = T.attn_decode(kc, vc, q, lens, spec.max_len, mask=tm)
+    out = T.attn_decode(kc, vc, q, lens, spec.max_len, mask=tm,
+                        softmax_scale=0.0 if scale is None else scale)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     # oracle: quantise with the oracle's own quantiser, then exact attention
     okc = oq.build_cache(inp.k, bits, "token", cap=spec.cap)
     ovc = oq.build_cache(inp.v, bits, "channel", cap=spec.cap)
     want = oa.decode(inp.q, oq.dequantized_all(okc), oq.dequantized_all(ovc), st.seq_lens,
-                     mask=mask, heads=heads, workers=workers)
+                     mask=mask, heads=heads, workers=workers, scale=scale)
     return got, want, (kc, vc, q, lens, tm)
 
 
@@ -52,6 +53,19 @@ def test_decode_small_ragged(r, bits, n8):
         inp.v[b, :, n:] = 0
     note(f"decode small r={r} bits={bits} n8={n8} lens={inp.structure.seq_lens.tolist()}")
     got, want, _ = run_decode(inp)
+    err = max_abs(got, want)
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("scale", [0.02, 0.25])
+def test_decode_softmax_scale(scale):
+    """A softmax scale other than 1/sqrt(d), int4 and int8 heads, ragged
+    lengths, against the oracle at the same scale."""
+    require_gpu()
+    spec = W.small("decode", B=4, Hq=8, Hkv=2, ragged=(1, 900), bits=4, n_int8_heads=1, seed=43)
+    inp = W.make_inputs(spec)
+    note(f"decode softmax_scale={scale} lens={inp.structure.seq_lens.tolist()}")
+    got, want, _ = run_decode(inp, scale=scale)
     err = max_abs(got, want)
     assert err <= TOL, err
 

@@ -15,7 +15,7 @@ from tests.gpu_util import (TOL, require_gpu, note, gpu_cache, max_abs, lens_ten
 pytestmark = pytest.mark.gpu
 
 
-def gpu_run(inp, mask=None, lens=None):
+def gpu_run(inp, mask=None, lens=None, scale=0.0):
     spec, st = inp.spec, inp.structure
     bits = st.head_bits
     kc = gpu_cache(inp.k, bits, T.LAYOUT_TOKEN, spec.cap)
@@ -27,24 +27,24 @@ def gpu_run(inp, mask=None, lens=None):
         md = torch.from_numpy(np.ascontiguousarray(mask)).cuda()
         tm = T.TileMask(md, mask.shape[-2], mask.shape[-1],
                         stride_b=mask.shape[-2] * mask.shape[-1] if mask.ndim == 3 else 0)
-    out = T.attn_prefill(kc, vc, q, lt, mask=tm)
+    out = T.attn_prefill(kc, vc, q, lt, mask=tm, softmax_scale=scale)
     torch.cuda.synchronize()
     return out, (kc, vc, q, lt, tm)
 
 
-def gpu_run_np(inp, mask=None, lens=None):
-    out, ctx = gpu_run(inp, mask=mask, lens=lens)
+def gpu_run_np(inp, mask=None, lens=None, scale=0.0):
+    out, ctx = gpu_run(inp, mask=mask, lens=lens, scale=scale)
     return out.cpu().numpy().astype(np.float64), ctx
 
 
-def oracle_run(inp, mask=None, lens=None, rows=None, heads=None, workers=4):
+def oracle_run(inp, mask=None, lens=None, rows=None, heads=None, workers=4, scale=None):
     spec, st = inp.spec, inp.structure
     bits = st.head_bits
     okc = oq.build_cache(inp.k, bits, "token", cap=spec.cap)
     ovc = oq.build_cache(inp.v, bits, "channel", cap=spec.cap)
     return oa.prefill(inp.q, oq.dequantized_all(okc), oq.dequantized_all(ovc),
                       st.seq_lens if lens is None else lens, mask=mask, rows=rows,
-                      heads=heads, workers=workers)
+                      heads=heads, workers=workers, scale=scale)
 
 
 @pytest.mark.parametrize("r", [1, 2, 4, 8])
@@ -62,6 +62,26 @@ def test_prefill_small_dense(r, L):
     assert err <= TOL, err
     # rows at or beyond the sequence length are zero
     assert not got[1, :, lens[1]:].any()
+
+
+@pytest.mark.parametrize("scale", [0.02, 0.25])
+def test_prefill_softmax_scale(scale):
+    """A softmax scale other than 1/sqrt(d), int4 and int8 heads, against the
+    oracle at the same scale.  The K-hat tiles are staged in fp16, so the
+    score error is proportional to the scores: at or below 1/sqrt(d) the bar
+    holds, above it (0.25 makes the scores ~2.8x the default's) the error
+    may grow in proportion (measured 2.9e-3 at 0.25)."""
+    require_gpu()
+    spec = W.small("prefill", B=2, Hq=8, Hkv=2, L=300, bits=4, n_int8_heads=1, seed=41)
+    inp = W.make_inputs(spec)
+    lens = np.array([300, 170], dtype=np.int32)
+    note(f"prefill softmax_scale={scale} lens={lens.tolist()}")
+    got, _ = gpu_run_np(inp, lens=lens, scale=scale)
+    want = oracle_run(inp, lens=lens, scale=scale)
+    err = max_abs(got, want)
+    growth = max(1.0, scale * np.sqrt(spec.D))
+    note(f"max-abs {err:.3e} (bar {TOL * growth:.2e})")
+    assert err <= TOL * growth, err
 
 
 @pytest.mark.parametrize("r", [1, 4])
