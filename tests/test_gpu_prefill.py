@@ -133,6 +133,30 @@ def test_prefill_masked(r):
     assert not got[1, :, 512:].any()
 
 
+@pytest.mark.parametrize("masked", [False, True])
+def test_prefill_batched_ragged_every_output(masked):
+    """Three entries of different lengths (3000, 2049, 700: ragged tails inside
+    a 64-key tile and a 128-row mask tile), int4 and int8 heads, GQA 4, with
+    and without a per-entry block mask (40% of the eligible tiles dropped):
+    every output against the oracle."""
+    require_gpu()
+    L = 3000
+    spec = W.small("prefill", B=3, Hq=8, Hkv=2, L=L, bits=4, n_int8_heads=1, seed=47)
+    inp = W.make_inputs(spec)
+    lens = np.array([3000, 2049, 700], dtype=np.int32)
+    mask = None
+    if masked:
+        rng = np.random.default_rng(48)
+        mask = np.stack([W.skip_mask(L, 0.4, rng) for _ in range(3)])
+    note(f"prefill batched ragged lens={lens.tolist()} masked={masked}")
+    got, _ = gpu_run_np(inp, mask=mask, lens=lens)
+    want = oracle_run(inp, mask=mask, lens=lens)
+    err = max_abs(got, want)
+    note(f"max-abs {err:.3e}")
+    assert err <= TOL, err
+    assert not got[1, :, 2049:].any() and not got[2, :, 700:].any()
+
+
 @pytest.mark.parametrize("r", [4, 1])
 def test_prefill_mask_long_dropped_runs(r):
     """A mask whose kept tiles are far apart: the query tiles of the second
