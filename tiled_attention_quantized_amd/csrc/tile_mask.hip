@@ -210,10 +210,13 @@ score_kernel(MaskGenArgs a, int nb) {
 // Selection: one wave per mask row (four rows per workgroup, no LDS and no
 // barriers).  Lane l holds the scores of candidates c = 64r + l (KV tile
 // j = c + 1) for r < RR, RR the power of two at or above ceil((i - 1) / 64).
-// The m lowest (score, j) pairs are found without sorting: scores become unsigned keys with the same order, a bitwise search
-// finds the m-th smallest key v (the largest v with fewer than m keys below
-// it), and among the keys equal to v a second search drops the lowest j
-// first.  Counts are ballots over the live candidates.
+// The m lowest (score, j) pairs are found without sorting: scores become
+// unsigned keys with the same order, a bitwise search finds the m-th smallest
+// key v (the largest v with fewer than m keys below it), and among the keys
+// equal to v a second search drops the lowest j first.  Each count is the
+// population of one compare's lane mask per register (one vector compare and
+// two scalar instructions): a count that also masked off the lanes past the
+// candidates took three vector instructions and ran the generator 8% slower.
 __device__ __forceinline__ uint64_t order_key(double v) {
   if (v == 0.0) v = 0.0;                         // -0 and +0 compare equal
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
@@ -223,13 +226,19 @@ __device__ __forceinline__ uint64_t order_key(double v) {
 template <int RR>
 __device__ __forceinline__ void select_row(const double* srow, int ncand, int m, int lane,
                                            uint8_t* row) {
+  // lanes past the candidates hold the largest key, which no search value
+  // exceeds and no selected value equals (scores are finite, so every real
+  // key is smaller), so the counts need no mask of live lanes
   uint64_t key[RR];
 #pragma unroll
-  for (int r = 0; r < RR; ++r) key[r] = order_key(srow[1 + min(64 * r + lane, ncand - 1)]);
+  for (int r = 0; r < RR; ++r) {
+    const uint64_t k = order_key(srow[1 + min(64 * r + lane, ncand - 1)]);
+    key[r] = 64 * r + lane < ncand ? k : ~0ull;
+  }
   auto count_below = [&](uint64_t t) {
     int cnt = 0;
 #pragma unroll
-    for (int r = 0; r < RR; ++r) cnt += __popcll(__ballot(64 * r + lane < ncand && key[r] < t));
+    for (int r = 0; r < RR; ++r) cnt += __popcll(__ballot(key[r] < t));
     return cnt;
   };
   uint64_t v = 0;
@@ -243,8 +252,7 @@ __device__ __forceinline__ void select_row(const double* srow, int ncand, int m,
     const int t = u | (1 << bit);
     int cnt = 0;
 #pragma unroll
-    for (int r = 0; r < RR; ++r)
-      cnt += __popcll(__ballot(64 * r + lane < ncand && key[r] == v && 64 * r + lane < t));
+    for (int r = 0; r < RR; ++r) cnt += __popcll(__ballot(key[r] == v && 64 * r + lane < t));
     if (cnt < need) u = t;
   }
 #pragma unroll
